@@ -1,0 +1,184 @@
+"""Host block manager model: free pool, reference counts, block tables.
+
+Test infrastructure only (see the package docstring).
+
+Plain-Python restatement of the bookkeeping the pages describe:
+
+* foundry "PagedAttention" ops page, *Concept*: memory is handed out one
+  fixed-size block at a time on demand; freed blocks go back to a shared pool.
+* same page, *How it works*: the new token goes into the sequence's current
+  block; when that block is full a fresh block is taken from the global free
+  pool and the block table is extended, so allocation follows the actual
+  length.  Sequences with identical content point their tables at the same
+  physical blocks and copy on write when they diverge.  An empty free pool is
+  the point where a scheduler would preempt (here: an error, state unchanged).
+* same page, *At a glance*: shared blocks are tracked by reference count and a
+  block is copied only when a sequence writes to it.
+* aiacademy lesson "Paged Attention": a new block is allocated only when decode
+  fills the last one, every block is released when the request completes, and
+  any free block fits any request.
+
+Readings where the pages are silent (the same contract the C library states):
+
+* the free pool is a stack; it starts as ``free_order`` with ``free_order[0]``
+  handed out first, and released blocks are pushed on top (reused first);
+* releasing a sequence walks its table in logical order;
+* on copy-on-write the writing sequence receives the new private block and the
+  other sharers keep the original (its count drops by one);
+* a block whose count is 1 is written in place, without a copy;
+* every failing call leaves the whole state unchanged.
+"""
+
+import copy
+
+
+class PoolExhausted(Exception):
+    """No free block left for a required allocation (state unchanged)."""
+
+
+class StateError(Exception):
+    """Unknown or duplicate sequence id, or another invalid request."""
+
+
+class BlockManagerModel:
+    def __init__(self, num_blocks, block_size, free_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise StateError("pool dimensions must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise StateError("free_order must be a permutation of the pool")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = list(reversed(order))  # top of stack = end of list
+        self.refcount = [0] * num_blocks
+        self.tables = {}
+        self.lens = {}
+
+    # -- helpers ---------------------------------------------------------
+    def _take(self):
+        if not self.free:
+            raise PoolExhausted()
+        blk = self.free.pop()
+        self.refcount[blk] = 1
+        return blk
+
+    def _release(self, blk):
+        self.refcount[blk] -= 1
+        if self.refcount[blk] == 0:
+            self.free.append(blk)
+
+    def _need(self, seq):
+        if seq not in self.tables:
+            raise StateError(f"unknown sequence {seq}")
+
+    def _atomic(self, fn):
+        saved = (list(self.free), list(self.refcount), copy.deepcopy(self.tables), dict(self.lens))
+        try:
+            return fn()
+        except Exception:
+            self.free, self.refcount, self.tables, self.lens = saved
+            raise
+
+    # -- operations -------------------------------------------------------
+    def create(self, seq, num_tokens):
+        """New sequence holding ``num_tokens`` tokens in ceil(n / bs) blocks."""
+        if seq in self.tables:
+            raise StateError(f"sequence {seq} exists")
+        if num_tokens < 0:
+            raise StateError("negative length")
+
+        def run():
+            nb = -(-num_tokens // self.block_size)
+            self.tables[seq] = [self._take() for _ in range(nb)]
+            self.lens[seq] = num_tokens
+
+        self._atomic(run)
+
+    def fork(self, parent, child):
+        """``child`` shares every block of ``parent``; counts go up by one."""
+        self._need(parent)
+        if child in self.tables:
+            raise StateError(f"sequence {child} exists")
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        for blk in self.tables[child]:
+            self.refcount[blk] += 1
+
+    def append(self, seq):
+        """Reserve the slot for one new token; returns ``(slot, pair)``.
+
+        ``pair`` is ``(src, dst)`` when the current block was shared and had to
+        be copied first, else ``None``.
+        """
+        self._need(seq)
+
+        def run():
+            pos = self.lens[seq]
+            table = self.tables[seq]
+            lb, off = divmod(pos, self.block_size)
+            pair = None
+            if off == 0:
+                table.append(self._take())
+            elif self.refcount[table[lb]] > 1:
+                src = table[lb]
+                dst = self._take()
+                self._release(src)
+                table[lb] = dst
+                pair = (src, dst)
+            self.lens[seq] = pos + 1
+            return table[lb] * self.block_size + off, pair
+
+        return self._atomic(run)
+
+    def append_batch(self, seqs):
+        """``append`` for each sequence in order; all-or-nothing."""
+        return self._atomic(lambda: [self.append(s) for s in seqs])
+
+    def cow(self, seq, logical_block):
+        """Give ``seq`` a private copy of one logical block if it is shared."""
+        self._need(seq)
+        table = self.tables[seq]
+        if not 0 <= logical_block < len(table):
+            raise StateError("logical block out of range")
+        src = table[logical_block]
+        if self.refcount[src] == 1:
+            return None
+
+        def run():
+            dst = self._take()
+            self._release(src)
+            table[logical_block] = dst
+            return (src, dst)
+
+        return self._atomic(run)
+
+    def release(self, seq):
+        """Return every block of ``seq`` to the pool (count drops by one each)."""
+        self._need(seq)
+        for blk in self.tables.pop(seq):
+            self._release(blk)
+        del self.lens[seq]
+
+    def slots(self, seq, start, count):
+        """Slots of logical positions ``start .. start+count-1`` of ``seq``."""
+        self._need(seq)
+        if start < 0 or count < 0 or start + count > self.lens[seq]:
+            raise StateError("positions outside the sequence")
+        table = self.tables[seq]
+        out = []
+        for pos in range(start, start + count):
+            lb, off = divmod(pos, self.block_size)
+            out.append(table[lb] * self.block_size + off)
+        return out
+
+    # -- inspection -------------------------------------------------------
+    def num_free(self):
+        return len(self.free)
+
+    def table(self, seq):
+        self._need(seq)
+        return list(self.tables[seq])
+
+    def length(self, seq):
+        self._need(seq)
+        return self.lens[seq]
