@@ -1,0 +1,232 @@
+/*
+ * pa.h -- C ABI of libpagedkv: the PagedAttention decode hot path on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the operations are (PagedAttention pages):
+ *   - foundry "PagedAttention" ops page, section "Concept": each sequence's KV
+ *     cache is cut into fixed-size blocks that can sit anywhere in GPU memory;
+ *     a per-sequence block table maps logical token positions to physical
+ *     blocks; blocks are handed out on demand and freed blocks return to a
+ *     shared pool.
+ *   - same page, "How it works": each decode step writes the new token's key
+ *     and value into the sequence's current block (pa_write_kv); a full block
+ *     means a fresh block from the free pool and one more table entry
+ *     (pa_seq_append); the attention kernel reads KV through the block table
+ *     (pa_decode); sequences with identical content share physical blocks and
+ *     copy on write when they diverge (pa_seq_cow / pa_copy_blocks); an empty
+ *     pool is where a scheduler preempts (PA_ENOMEM here).
+ *   - same page, "At a glance": shared blocks carry reference counts and a
+ *     block is copied only when a sequence writes to it.
+ *   - aiacademy lesson "Paged Attention", virtual-memory analogy table: token
+ *     positions are contiguous while physical blocks are scattered; a block is
+ *     allocated only when decode fills the last one.
+ *
+ * Layout conventions (the pages fix none of them; this header does):
+ *   - KV pools: k_cache and v_cache are each
+ *       [num_blocks][num_kv_heads][block_size][head_dim]
+ *     of the cache element type, densely packed; one (block, head) is one
+ *     contiguous run of block_size * head_dim elements.
+ *   - slot of a token = physical_block * block_size + offset_in_block (int64).
+ *   - block_tables: int32 [num_seqs][max_blocks_per_seq]; entry i is the
+ *     physical block of logical block i; entries at or past
+ *     ceil(context_len / block_size) are never read (pad them with -1).
+ *   - context_lens: int32 [num_seqs]; the number of tokens each query attends
+ *     to, including a token written earlier in the same step.
+ *   - grouped query heads: query head h reads KV head h / (num_q_heads /
+ *     num_kv_heads).
+ *   - decode output: out[s][h][:] = softmax(scale * q[s][h] . K_s^T) V_s over
+ *     the sequence's first context_lens[s] tokens; a sequence with length 0
+ *     yields zeros.
+ *   - bf16 is stored as its 16-bit pattern; fp32 accumulation throughout.
+ *
+ * Memory and ownership: every data pointer of a device call is a device
+ * pointer owned by the caller; the library never allocates, frees or
+ * synchronises.  Device calls are enqueued on `stream` (a hipStream_t passed
+ * as void*; NULL is the default stream) and return after enqueueing.
+ *
+ * Errors: every call returns a pa_status_t; no exception crosses the ABI.
+ * Argument errors visible on the host return PA_EINVAL or PA_EUNSUPPORTED and
+ * enqueue nothing.  A failed launch returns PA_EHIP.  pa_last_error() gives a
+ * message for the calling thread's last failure.  Values that live in device
+ * memory (slots, block ids, lengths, copy pairs) are preconditions: the
+ * kernels never read or write outside the buffers described by the host-side
+ * sizes, and the results for out-of-range values are stated per call.
+ *
+ * Threading: device entry points are thread-safe.  A pa_pool is not: callers
+ * serialise access to one pool.
+ */
+#ifndef PAGEDKV_PA_H
+#define PAGEDKV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,       /* bad argument (null pointer, size, shape)            */
+  PA_EUNSUPPORTED = 2, /* valid but not built (head_dim, dtype, group size)   */
+  PA_ENOMEM = 3,       /* free pool too small; pool state unchanged           */
+  PA_ESTATE = 4,       /* unknown / duplicate sequence id, bad pool request   */
+  PA_EHIP = 5          /* HIP runtime error while launching                   */
+} pa_status_t;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype_t;
+
+/* Shape of a pair of KV pools.  dtype is a pa_dtype_t. */
+typedef struct {
+  int32_t num_blocks;   /* physical blocks in each pool, > 0                 */
+  int32_t block_size;   /* tokens per block: a power of two in [1, 256]      */
+  int32_t num_kv_heads; /* > 0                                               */
+  int32_t head_dim;     /* 64, 128 or 256                                    */
+  int32_t dtype;        /* PA_F32 or PA_BF16                                 */
+} pa_cache_t;
+
+/* Library version string, e.g. "pagedkv 0.1 gfx950". */
+const char *pa_version(void);
+
+/* Message for the calling thread's most recent non-OK status. */
+const char *pa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * pa_write_kv -- store new tokens' keys and values into their slots.
+ * (foundry PagedAttention page, "How it works": the new token's key and
+ * value go into the sequence's current block.)
+ *
+ *   k, v          device [num_tokens][num_kv_heads][head_dim], cache dtype
+ *   slot_mapping  device int64 [num_tokens]; token i goes to block
+ *                 slot / block_size, offset slot % block_size, for every
+ *                 KV head.  slot < 0 means padding: nothing is written.
+ *                 Slots >= num_blocks * block_size are skipped as well.
+ *   k_cache, v_cache  device pools described by *cache.
+ * Distinct tokens must name distinct slots (otherwise the stored row is one
+ * of the writers', unspecified which).  num_tokens == 0 is a no-op.
+ * Bytes are copied unchanged: the result is bitwise the input rows.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_write_kv(const void *k, const void *v, const int64_t *slot_mapping,
+                        int32_t num_tokens, void *k_cache, void *v_cache,
+                        const pa_cache_t *cache, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_copy_blocks -- duplicate whole blocks for copy-on-write.
+ * (foundry PagedAttention page, "How it works" and "At a glance": a shared
+ * block is copied only when a sequence writes to it.)
+ *
+ *   src_dst_pairs  device int64 [num_pairs][2] of (src, dst) block ids.
+ * Every KV head and every slot of block src is copied to block dst, in both
+ * pools.  Preconditions: all dst distinct and no dst is also a src (then the
+ * result equals copying from a snapshot, in any order).  Pairs with an id
+ * outside [0, num_blocks) are skipped.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cache_t *cache,
+                           const int64_t *src_dst_pairs, int32_t num_pairs, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode -- single-query paged decode attention.
+ * (foundry PagedAttention page, "How it works": the attention kernel reads
+ * KV through the block table, gathering scattered blocks, so non-contiguous
+ * storage leaves the math unchanged.)
+ *
+ *   q             device [num_seqs][num_q_heads][head_dim], cache dtype
+ *   k_cache, v_cache, *cache   the pools (as above)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  device int32 [num_seqs]
+ *   max_context_len  host bound >= every context_lens[s]; sizes the launch.
+ *                 Lengths are clamped to min(max_context_len,
+ *                 max_blocks_per_seq * block_size).
+ *   scale         softmax scale (usually 1/sqrt(head_dim))
+ *   partition_size 0: one pass per (sequence, KV head).  Otherwise a multiple
+ *                 of block_size: each (sequence, KV head) context is split into
+ *                 partitions of that many tokens, processed in parallel and
+ *                 merged by a second kernel (online-softmax merge).
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes when partition_size > 0 (may be NULL otherwise); its
+ *                 contents on entry do not matter.
+ *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype
+ *                 (PA_F32, or the cache dtype).
+ * num_q_heads must be a multiple of num_kv_heads, with a ratio of 1, 2, 4 or
+ * 8.  Block ids outside [0, num_blocks) inside a sequence's length are a
+ * precondition violation: the kernel stays inside the pools but that
+ * sequence's output is unspecified.
+ * ------------------------------------------------------------------------ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
+                      const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t max_context_len, float scale,
+                      int32_t partition_size, void *workspace, size_t workspace_bytes,
+                      void *out, int32_t out_dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Host block manager (host memory only, no device calls).
+ * (foundry PagedAttention page, "Concept", "How it works", "At a glance";
+ * aiacademy lesson "Paged Attention", analogy table.)
+ *
+ * Policy fixed by this library where the pages leave it open:
+ *   - the free pool is a stack that starts as free_order (free_order[0] is
+ *     handed out first; NULL means 0, 1, 2, ...); released blocks are pushed
+ *     on top and handed out next;
+ *   - a sequence holds exactly ceil(len / block_size) blocks;
+ *   - appending to a block whose reference count is > 1 first moves the
+ *     writer to a fresh private copy (the pair (src, dst) is reported for
+ *     pa_copy_blocks); the other sharers keep src;
+ *   - releasing a sequence walks its table in logical order;
+ *   - every failing call leaves the pool unchanged.
+ * Sequence ids are arbitrary int64 values chosen by the caller.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_pool pa_pool;
+
+/* Create a pool; *out receives the handle (owned by the caller until
+ * pa_pool_destroy).  free_order: host int32 [num_blocks] permutation or NULL. */
+pa_status_t pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order,
+                           pa_pool **out);
+void pa_pool_destroy(pa_pool *pool);
+
+int32_t pa_pool_num_free(const pa_pool *pool);
+/* Reference count of a block, or -1 for an id outside the pool. */
+int32_t pa_pool_refcount(const pa_pool *pool, int32_t block);
+/* Free blocks in hand-out order into host out[cap]; *n receives the count. */
+pa_status_t pa_pool_free_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n);
+
+/* New sequence with num_tokens tokens (ceil(n / block_size) fresh blocks). */
+pa_status_t pa_seq_create(pa_pool *pool, int64_t seq, int32_t num_tokens);
+/* child shares every block of parent (reference counts + 1). */
+pa_status_t pa_seq_fork(pa_pool *pool, int64_t parent, int64_t child);
+/* Reserve the slot of one new token of seq.  *slot receives it; cow_pair[2]
+ * receives (src, dst) when a shared block had to be copied first, else
+ * (-1, -1). */
+pa_status_t pa_seq_append(pa_pool *pool, int64_t seq, int64_t *slot, int64_t cow_pair[2]);
+/* pa_seq_append for seqs[0..n) in order, all or nothing.  slots: host int64
+ * [n]; pairs: host int64 [n][2] receives the copy pairs in order, *num_pairs
+ * their count (at most n). */
+pa_status_t pa_seq_append_batch(pa_pool *pool, const int64_t *seqs, int32_t n, int64_t *slots,
+                                int64_t *pairs, int32_t *num_pairs);
+/* Give seq a private copy of logical block lb if it is shared: pair (src,
+ * dst), else (-1, -1) and nothing changes. */
+pa_status_t pa_seq_cow(pa_pool *pool, int64_t seq, int32_t logical_block, int64_t pair[2]);
+/* Release every block of seq (counts - 1; blocks reaching 0 return to the
+ * pool) and forget seq. */
+pa_status_t pa_seq_free(pa_pool *pool, int64_t seq);
+/* Slots of logical positions [start, start + count) of seq into host
+ * slots[count]. */
+pa_status_t pa_seq_slots(const pa_pool *pool, int64_t seq, int32_t start, int32_t count,
+                         int64_t *slots);
+/* Table row of seq into host row[max_blocks] (padded with -1), plus its block
+ * count and length.  PA_EINVAL if the row does not fit. */
+pa_status_t pa_seq_table(const pa_pool *pool, int64_t seq, int32_t *row, int32_t max_blocks,
+                         int32_t *num_blocks, int32_t *len);
+/* Tables and lengths of seqs[0..n) into host tables[n][max_blocks] (padded
+ * with -1) and context_lens[n], ready to upload for pa_decode. */
+pa_status_t pa_pool_tables(const pa_pool *pool, const int64_t *seqs, int32_t n, int32_t *tables,
+                           int32_t max_blocks, int32_t *context_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_PA_H */

@@ -1,0 +1,407 @@
+"""Python binding of libpagedkv (PagedAttention decode hot path, MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP library
+``libpagedkv.so`` built next to this file (``python -m
+paged_kv_cache_354_amd.build``).  There is no fallback: if the library is
+missing, every call raises.  PyTorch supplies device memory and streams.
+
+The functions carry the C names declared in ``include/pa.h``:
+
+* ``pa_write_kv``     -- new tokens' K/V into their slots
+* ``pa_copy_blocks``  -- whole-block copies for copy-on-write
+* ``pa_decode``       -- paged single-query decode attention
+* ``pa_decode_workspace_bytes``
+* ``pa_pool_*`` / ``pa_seq_*`` -- host block manager (free pool, reference
+  counts, block tables, copy-on-write decisions)
+
+Device arguments are torch tensors on the GPU (contiguous, the documented
+dtypes and shapes); they are checked here against the cache descriptor so
+that no launch can address memory outside the tensors.  The stream defaults
+to torch's current stream.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ENOMEM, PA_ESTATE, PA_EHIP = range(6)
+PA_F32, PA_BF16 = 0, 1
+
+_STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "ESTATE", 5: "EHIP"}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class PoolExhausted(PagedKVError):
+    """PA_ENOMEM from the block manager: no free block, state unchanged."""
+
+
+class PoolStateError(PagedKVError):
+    """PA_ESTATE from the block manager."""
+
+
+class PaCache(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+_i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+_P32, _P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_write_kv": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp, _i32,
+                         ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
+    "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
+    "pa_pool_destroy": (None, [_vp]),
+    "pa_pool_num_free": (_i32, [_vp]),
+    "pa_pool_refcount": (_i32, [_vp, _i32]),
+    "pa_pool_free_list": (_i32, [_vp, _P32, _i32, _P32]),
+    "pa_seq_create": (_i32, [_vp, _i64, _i32]),
+    "pa_seq_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_seq_append": (_i32, [_vp, _i64, _P64, _P64]),
+    "pa_seq_append_batch": (_i32, [_vp, _P64, _i32, _P64, _P64, _P32]),
+    "pa_seq_cow": (_i32, [_vp, _i64, _i32, _P64]),
+    "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _P64]),
+    "pa_seq_table": (_i32, [_vp, _i64, _P32, _i32, _P32, _P32]),
+    "pa_pool_tables": (_i32, [_vp, _P64, _i32, _P32, _i32, _P32]),
+}
+
+EXPORTED = tuple(_SIGS)
+
+
+def load():
+    """Load libpagedkv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m paged_kv_cache_354_amd.build` "
+                               "(there is no non-HIP fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status, cls=PagedKVError):
+    if status != PA_OK:
+        msg = load().pa_last_error().decode()
+        if status == PA_ENOMEM:
+            raise PoolExhausted(status, msg)
+        if status == PA_ESTATE:
+            raise PoolStateError(status, msg)
+        raise cls(status, msg)
+
+
+def pa_version():
+    return load().pa_version().decode()
+
+
+# --- device calls ----------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_desc(k_cache):
+    """Descriptor of a pool tensor ``[num_blocks][num_kv_heads][block_size][head_dim]``."""
+    nb, hkv, bs, d = k_cache.shape
+    return PaCache(nb, bs, hkv, d, _dtype_code(k_cache))
+
+
+def _pools(k_cache, v_cache):
+    if k_cache.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    desc = cache_desc(k_cache)
+    kp = _dev(k_cache, "k_cache")
+    vp = _dev(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    return desc, kp, vp
+
+
+def pa_write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """Store token i's K/V ``[T][Hkv][d]`` at ``slot_mapping[i]`` (int64; < 0 skips)."""
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    t = int(slot_mapping.shape[0])
+    shape = (t, desc.num_kv_heads, desc.head_dim)
+    _check(load().pa_write_kv(_dev(k, "k", k_cache.dtype, shape), _dev(v, "v", k_cache.dtype, shape),
+                              _dev(slot_mapping, "slot_mapping", torch.int64, (t,)), t, kp, vp,
+                              ctypes.byref(desc), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
+    """Copy block ``src`` to ``dst`` in both pools for each int64 (src, dst) row."""
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    n = int(src_dst_pairs.shape[0])
+    if n == 0:
+        return
+    _check(load().pa_copy_blocks(kp, vp, ctypes.byref(desc),
+                                 _dev(src_dst_pairs, "src_dst_pairs", torch.int64, (n, 2)), n,
+                                 _stream(stream)))
+
+
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                partition_size))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+              partition_size=0, workspace=None, out=None, out_dtype=None, stream=None):
+    """Paged decode attention; returns ``out [B][Hq][d]``.
+
+    ``q [B][Hq][d]`` in the cache dtype; ``block_tables int32 [B][MB]``;
+    ``context_lens int32 [B]``; ``max_context_len`` a host int bounding every
+    length; ``partition_size`` 0 or a multiple of the block size (then a
+    uint8 ``workspace`` of ``pa_decode_workspace_bytes`` bytes is needed; one
+    is allocated here if not given).
+    """
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    b, hq, d = q.shape
+    if d != desc.head_dim:
+        raise ValueError("q head_dim does not match the pools")
+    qp = _dev(q, "q", k_cache.dtype)
+    mb = int(block_tables.shape[1]) if block_tables.dim() == 2 else -1
+    tp = _dev(block_tables, "block_tables", torch.int32, (b, mb))
+    lp = _dev(context_lens, "context_lens", torch.int32, (b,))
+    if out_dtype is None:
+        out_dtype = q.dtype if out is None else out.dtype
+    if out is None:
+        out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
+    op = _dev(out, "out", out_dtype, (b, hq, d))
+    ws_need = pa_decode_workspace_bytes(b, hq, d, int(max_context_len), int(partition_size))
+    if partition_size and workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        wp = _dev(workspace, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    else:
+        wp, wbytes = ctypes.c_void_p(0), 0
+    _check(load().pa_decode(qp, b, hq, kp, vp, ctypes.byref(desc), tp, mb, lp, int(max_context_len),
+                            float(scale), int(partition_size), wp, wbytes, op, _dtype_code(out),
+                            _stream(stream)))
+    return out
+
+
+# --- host block manager ------------------------------------------------------------
+
+def _np_ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def pa_pool_create(num_blocks, block_size, free_order=None):
+    handle = ctypes.c_void_p()
+    order = None
+    if free_order is not None:
+        arr = np.ascontiguousarray(free_order, dtype=np.int32)
+        if arr.shape != (num_blocks,):
+            raise ValueError("free_order must have num_blocks entries")
+        order = _np_ptr(arr, ctypes.c_int32)
+    _check(load().pa_pool_create(num_blocks, block_size, order, ctypes.byref(handle)))
+    return handle
+
+
+def pa_pool_destroy(pool):
+    load().pa_pool_destroy(pool)
+
+
+def pa_pool_num_free(pool):
+    return int(load().pa_pool_num_free(pool))
+
+
+def pa_pool_refcount(pool, block):
+    return int(load().pa_pool_refcount(pool, block))
+
+
+def pa_pool_free_list(pool):
+    n = pa_pool_num_free(pool)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(load().pa_pool_free_list(pool, _np_ptr(out, ctypes.c_int32), n, ctypes.byref(got)))
+    return out[:got.value]
+
+
+def pa_seq_create(pool, seq, num_tokens):
+    _check(load().pa_seq_create(pool, seq, num_tokens))
+
+
+def pa_seq_fork(pool, parent, child):
+    _check(load().pa_seq_fork(pool, parent, child))
+
+
+def pa_seq_append(pool, seq):
+    """Returns ``(slot, pair)``; ``pair`` is (src, dst) or None."""
+    slot = ctypes.c_int64()
+    pair = (ctypes.c_int64 * 2)()
+    _check(load().pa_seq_append(pool, seq, ctypes.byref(slot), pair))
+    return slot.value, (None if pair[0] < 0 else (pair[0], pair[1]))
+
+
+def pa_seq_append_batch(pool, seqs):
+    """Returns ``(slots int64 [n], pairs int64 [k][2])``; all or nothing."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    n = s.shape[0]
+    slots = np.empty(max(n, 1), dtype=np.int64)
+    pairs = np.empty((max(n, 1), 2), dtype=np.int64)
+    k = ctypes.c_int32()
+    _check(load().pa_seq_append_batch(pool, _np_ptr(s, ctypes.c_int64), n,
+                                      _np_ptr(slots, ctypes.c_int64), _np_ptr(pairs, ctypes.c_int64),
+                                      ctypes.byref(k)))
+    return slots[:n], pairs[:k.value]
+
+
+def pa_seq_cow(pool, seq, logical_block):
+    pair = (ctypes.c_int64 * 2)()
+    _check(load().pa_seq_cow(pool, seq, logical_block, pair))
+    return None if pair[0] < 0 else (pair[0], pair[1])
+
+
+def pa_seq_free(pool, seq):
+    _check(load().pa_seq_free(pool, seq))
+
+
+def pa_seq_slots(pool, seq, start, count):
+    out = np.empty(max(count, 1), dtype=np.int64)
+    _check(load().pa_seq_slots(pool, seq, start, count, _np_ptr(out, ctypes.c_int64)))
+    return out[:count]
+
+
+def pa_seq_table(pool, seq, max_blocks=None):
+    """Returns ``(row int32 [nb], length)``."""
+    lib = load()
+    nb, ln = ctypes.c_int32(), ctypes.c_int32()
+    if max_blocks is None:
+        # a zero-capacity call reports the block count (EINVAL if it is > 0)
+        st = lib.pa_seq_table(pool, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln))
+        if st not in (PA_OK, PA_EINVAL):
+            _check(st)
+        max_blocks = nb.value
+    row = np.empty(max(max_blocks, 1), dtype=np.int32)
+    _check(lib.pa_seq_table(pool, seq, _np_ptr(row, ctypes.c_int32), max_blocks, ctypes.byref(nb),
+                            ctypes.byref(ln)))
+    return row[:nb.value].copy(), ln.value
+
+
+def pa_pool_tables(pool, seqs, max_blocks, tables=None, context_lens=None):
+    """Fill ``tables int32 [n][max_blocks]`` (-1 padded) and ``context_lens int32 [n]``."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    n = s.shape[0]
+    if tables is None:
+        tables = np.empty((n, max_blocks), dtype=np.int32)
+    if context_lens is None:
+        context_lens = np.empty(n, dtype=np.int32)
+    if tables.shape != (n, max_blocks) or tables.dtype != np.int32 or not tables.flags.c_contiguous:
+        raise ValueError("tables must be C-contiguous int32 [n][max_blocks]")
+    if context_lens.shape != (n,) or context_lens.dtype != np.int32:
+        raise ValueError("context_lens must be int32 [n]")
+    _check(load().pa_pool_tables(pool, _np_ptr(s, ctypes.c_int64), n, _np_ptr(tables, ctypes.c_int32),
+                                 max_blocks, _np_ptr(context_lens, ctypes.c_int32)))
+    return tables, context_lens
+
+
+class BlockPool:
+    """Owning wrapper of a ``pa_pool`` handle with the C calls as methods."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.handle = pa_pool_create(num_blocks, block_size, free_order)
+
+    def close(self):
+        if self.handle:
+            pa_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def create(self, seq, n):
+        pa_seq_create(self.handle, seq, n)
+
+    def fork(self, parent, child):
+        pa_seq_fork(self.handle, parent, child)
+
+    def append(self, seq):
+        return pa_seq_append(self.handle, seq)
+
+    def append_batch(self, seqs):
+        return pa_seq_append_batch(self.handle, seqs)
+
+    def cow(self, seq, logical_block):
+        return pa_seq_cow(self.handle, seq, logical_block)
+
+    def release(self, seq):
+        pa_seq_free(self.handle, seq)
+
+    def slots(self, seq, start, count):
+        return pa_seq_slots(self.handle, seq, start, count)
+
+    def table(self, seq):
+        return pa_seq_table(self.handle, seq)[0]
+
+    def length(self, seq):
+        return pa_seq_table(self.handle, seq)[1]
+
+    def refcount(self, block):
+        return pa_pool_refcount(self.handle, block)
+
+    def num_free(self):
+        return pa_pool_num_free(self.handle)
+
+    def free_order(self):
+        return pa_pool_free_list(self.handle)
+
+    def tables(self, seqs, max_blocks, tables=None, context_lens=None):
+        return pa_pool_tables(self.handle, seqs, max_blocks, tables, context_lens)

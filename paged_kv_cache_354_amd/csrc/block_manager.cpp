@@ -1,0 +1,307 @@
+// Host block manager: free pool, reference counts, per-sequence block tables.
+//
+// foundry "PagedAttention" ops page:
+//   * Concept -- blocks are handed out one at a time on demand; freed blocks
+//     return to a shared pool; waste is at most one partly filled block per
+//     sequence.
+//   * How it works -- the new token goes into the current block; a full block
+//     means a fresh block from the global free pool and a longer block table;
+//     sequences with identical content point at the same physical blocks and
+//     copy on write when they diverge; an empty pool is where a scheduler
+//     preempts.
+//   * At a glance -- sharing is tracked by reference counts; a block is copied
+//     only when a sequence writes to it.
+// aiacademy lesson "Paged Attention", analogy table -- a block is allocated only
+// when decode fills the last one; any free block fits any request.
+//
+// Policy (the pages leave it open): the free pool is a LIFO stack seeded with
+// free_order so that free_order[0] is handed out first; release walks a table
+// in logical order; the writer of a shared block gets the private copy.  Every
+// call either succeeds or leaves the pool untouched.
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa.h"
+#include "pa_status.h"
+
+namespace {
+
+struct Seq {
+  std::vector<int32_t> table;
+  int64_t len = 0;
+};
+
+}  // namespace
+
+struct pa_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // back() is handed out next
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t take() {
+    int32_t b = free_stack.back();
+    free_stack.pop_back();
+    refcount[b] = 1;
+    return b;
+  }
+  void release(int32_t b) {
+    if (--refcount[b] == 0) free_stack.push_back(b);
+  }
+  // Blocks one append to `s` needs: 1 for a fresh or copied block, else 0.
+  int32_t append_need(const Seq &s) const {
+    int64_t off = s.len % block_size;
+    if (off == 0) return 1;
+    return refcount[s.table[s.len / block_size]] > 1 ? 1 : 0;
+  }
+  // Performs one append; the caller has checked that a block is available.
+  void append(Seq &s, int64_t *slot, int64_t pair[2]) {
+    int64_t lb = s.len / block_size, off = s.len % block_size;
+    pair[0] = pair[1] = -1;
+    if (off == 0) {
+      s.table.push_back(take());
+    } else if (refcount[s.table[lb]] > 1) {
+      int32_t src = s.table[lb];
+      int32_t dst = take();
+      release(src);
+      s.table[lb] = dst;
+      pair[0] = src;
+      pair[1] = dst;
+    }
+    *slot = (int64_t)s.table[lb] * block_size + off;
+    s.len += 1;
+  }
+};
+
+using pa::fail;
+
+extern "C" {
+
+pa_status_t pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t *free_order,
+                           pa_pool **out) {
+  if (!out) return fail(PA_EINVAL, "pa_pool_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0)
+    return fail(PA_EINVAL, "pa_pool_create: num_blocks=%d block_size=%d must be > 0", num_blocks,
+                block_size);
+  pa_pool *p = new (std::nothrow) pa_pool;
+  if (!p) return fail(PA_ENOMEM, "pa_pool_create: host allocation failed");
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->refcount.assign(num_blocks, 0);
+  p->free_stack.resize(num_blocks);
+  std::vector<char> seen(num_blocks, 0);
+  for (int32_t i = 0; i < num_blocks; ++i) {
+    int32_t b = free_order ? free_order[i] : i;
+    if (b < 0 || b >= num_blocks || seen[b]) {
+      delete p;
+      return fail(PA_EINVAL, "pa_pool_create: free_order is not a permutation (entry %d = %d)", i,
+                  b);
+    }
+    seen[b] = 1;
+    p->free_stack[num_blocks - 1 - i] = b;
+  }
+  *out = p;
+  return PA_OK;
+}
+
+void pa_pool_destroy(pa_pool *pool) { delete pool; }
+
+int32_t pa_pool_num_free(const pa_pool *pool) {
+  return pool ? (int32_t)pool->free_stack.size() : -1;
+}
+
+int32_t pa_pool_refcount(const pa_pool *pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->refcount[block];
+}
+
+pa_status_t pa_pool_free_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n) {
+  if (!pool || !n) return fail(PA_EINVAL, "pa_pool_free_list: NULL argument");
+  int32_t total = (int32_t)pool->free_stack.size();
+  *n = total;
+  if (total > cap || (total > 0 && !out))
+    return fail(PA_EINVAL, "pa_pool_free_list: %d free blocks do not fit in %d", total, cap);
+  for (int32_t i = 0; i < total; ++i) out[i] = pool->free_stack[total - 1 - i];
+  return PA_OK;
+}
+
+pa_status_t pa_seq_create(pa_pool *pool, int64_t seq, int32_t num_tokens) {
+  if (!pool) return fail(PA_EINVAL, "pa_seq_create: pool is NULL");
+  if (num_tokens < 0) return fail(PA_EINVAL, "pa_seq_create: num_tokens=%d < 0", num_tokens);
+  if (pool->seqs.count(seq)) return fail(PA_ESTATE, "pa_seq_create: sequence %lld exists", (long long)seq);
+  int64_t need = ((int64_t)num_tokens + pool->block_size - 1) / pool->block_size;
+  if (need > (int64_t)pool->free_stack.size())
+    return fail(PA_ENOMEM, "pa_seq_create: %lld blocks needed, %zu free", (long long)need,
+                pool->free_stack.size());
+  Seq s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(pool->take());
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status_t pa_seq_fork(pa_pool *pool, int64_t parent, int64_t child) {
+  if (!pool) return fail(PA_EINVAL, "pa_seq_fork: pool is NULL");
+  auto it = pool->seqs.find(parent);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_fork: unknown sequence %lld", (long long)parent);
+  if (pool->seqs.count(child)) return fail(PA_ESTATE, "pa_seq_fork: sequence %lld exists", (long long)child);
+  Seq s = it->second;
+  for (int32_t b : s.table) pool->refcount[b] += 1;
+  pool->seqs.emplace(child, std::move(s));
+  return PA_OK;
+}
+
+pa_status_t pa_seq_append(pa_pool *pool, int64_t seq, int64_t *slot, int64_t cow_pair[2]) {
+  if (!pool || !slot || !cow_pair) return fail(PA_EINVAL, "pa_seq_append: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_append: unknown sequence %lld", (long long)seq);
+  if (pool->append_need(it->second) > (int32_t)pool->free_stack.size())
+    return fail(PA_ENOMEM, "pa_seq_append: free pool is empty");
+  pool->append(it->second, slot, cow_pair);
+  return PA_OK;
+}
+
+pa_status_t pa_seq_append_batch(pa_pool *pool, const int64_t *seqs, int32_t n, int64_t *slots,
+                                int64_t *pairs, int32_t *num_pairs) {
+  if (!pool || !num_pairs || n < 0 || (n > 0 && (!seqs || !slots || !pairs)))
+    return fail(PA_EINVAL, "pa_seq_append_batch: bad argument");
+  *num_pairs = 0;
+  std::vector<Seq *> refs(n);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PA_ESTATE, "pa_seq_append_batch: unknown sequence %lld", (long long)seqs[i]);
+    refs[i] = &it->second;
+  }
+  // Dry run on counts only, so that a shortage is found before anything
+  // changes.  A repeated sequence sees its own earlier appends.
+  {
+    std::unordered_map<int64_t, int64_t> extra_len;   // appends so far per seq
+    std::unordered_map<int64_t, char> private_tail;   // tail block already private
+    std::unordered_map<int32_t, int32_t> rc_drop;     // shared tails left so far
+    int64_t need = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const Seq &s = *refs[i];
+      int64_t len = s.len + extra_len[seqs[i]];
+      int64_t off = len % pool->block_size;
+      if (off == 0) {
+        need += 1;
+        private_tail[seqs[i]] = 1;
+      } else if (!private_tail[seqs[i]]) {
+        int32_t b = s.table[len / pool->block_size];
+        if (pool->refcount[b] - rc_drop[b] > 1) {
+          need += 1;
+          rc_drop[b] += 1;
+        }
+        private_tail[seqs[i]] = 1;
+      }
+      extra_len[seqs[i]] += 1;
+    }
+    if (need > (int64_t)pool->free_stack.size())
+      return fail(PA_ENOMEM, "pa_seq_append_batch: %lld blocks needed, %zu free", (long long)need,
+                  pool->free_stack.size());
+  }
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t pair[2];
+    pool->append(*refs[i], &slots[i], pair);
+    if (pair[0] >= 0) {
+      pairs[2 * np] = pair[0];
+      pairs[2 * np + 1] = pair[1];
+      ++np;
+    }
+  }
+  *num_pairs = np;
+  return PA_OK;
+}
+
+pa_status_t pa_seq_cow(pa_pool *pool, int64_t seq, int32_t logical_block, int64_t pair[2]) {
+  if (!pool || !pair) return fail(PA_EINVAL, "pa_seq_cow: NULL argument");
+  pair[0] = pair[1] = -1;
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_cow: unknown sequence %lld", (long long)seq);
+  Seq &s = it->second;
+  if (logical_block < 0 || logical_block >= (int32_t)s.table.size())
+    return fail(PA_ESTATE, "pa_seq_cow: logical block %d outside [0, %zu)", logical_block,
+                s.table.size());
+  int32_t src = s.table[logical_block];
+  if (pool->refcount[src] == 1) return PA_OK;
+  if (pool->free_stack.empty()) return fail(PA_ENOMEM, "pa_seq_cow: free pool is empty");
+  int32_t dst = pool->take();
+  pool->release(src);
+  s.table[logical_block] = dst;
+  pair[0] = src;
+  pair[1] = dst;
+  return PA_OK;
+}
+
+pa_status_t pa_seq_free(pa_pool *pool, int64_t seq) {
+  if (!pool) return fail(PA_EINVAL, "pa_seq_free: pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_free: unknown sequence %lld", (long long)seq);
+  for (int32_t b : it->second.table) pool->release(b);
+  pool->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status_t pa_seq_slots(const pa_pool *pool, int64_t seq, int32_t start, int32_t count,
+                         int64_t *slots) {
+  if (!pool || (count > 0 && !slots)) return fail(PA_EINVAL, "pa_seq_slots: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_slots: unknown sequence %lld", (long long)seq);
+  const Seq &s = it->second;
+  if (start < 0 || count < 0 || (int64_t)start + count > s.len)
+    return fail(PA_ESTATE, "pa_seq_slots: positions [%d, %d) outside length %lld", start,
+                start + count, (long long)s.len);
+  for (int32_t i = 0; i < count; ++i) {
+    int64_t pos = (int64_t)start + i;
+    slots[i] = (int64_t)s.table[pos / pool->block_size] * pool->block_size + pos % pool->block_size;
+  }
+  return PA_OK;
+}
+
+pa_status_t pa_seq_table(const pa_pool *pool, int64_t seq, int32_t *row, int32_t max_blocks,
+                         int32_t *num_blocks, int32_t *len) {
+  if (!pool || !num_blocks || !len) return fail(PA_EINVAL, "pa_seq_table: NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_table: unknown sequence %lld", (long long)seq);
+  const Seq &s = it->second;
+  *num_blocks = (int32_t)s.table.size();
+  *len = (int32_t)s.len;
+  if ((int32_t)s.table.size() > max_blocks || (max_blocks > 0 && !row))
+    return fail(PA_EINVAL, "pa_seq_table: %zu blocks do not fit in %d", s.table.size(), max_blocks);
+  for (int32_t i = 0; i < max_blocks; ++i) row[i] = i < (int32_t)s.table.size() ? s.table[i] : -1;
+  return PA_OK;
+}
+
+pa_status_t pa_pool_tables(const pa_pool *pool, const int64_t *seqs, int32_t n, int32_t *tables,
+                           int32_t max_blocks, int32_t *context_lens) {
+  if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables || !context_lens)))
+    return fail(PA_EINVAL, "pa_pool_tables: bad argument");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PA_ESTATE, "pa_pool_tables: unknown sequence %lld", (long long)seqs[i]);
+    if ((int32_t)it->second.table.size() > max_blocks)
+      return fail(PA_EINVAL, "pa_pool_tables: sequence %lld has %zu blocks > %d", (long long)seqs[i],
+                  it->second.table.size(), max_blocks);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq &s = pool->seqs.find(seqs[i])->second;
+    int32_t *row = tables + (int64_t)i * max_blocks;
+    int32_t nb = (int32_t)s.table.size();
+    if (nb) std::memcpy(row, s.table.data(), sizeof(int32_t) * nb);
+    for (int32_t j = nb; j < max_blocks; ++j) row[j] = -1;
+    context_lens[i] = (int32_t)s.len;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

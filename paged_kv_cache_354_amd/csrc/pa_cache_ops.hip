@@ -1,0 +1,121 @@
+// KV-slot write and whole-block copy for the paged KV pools (gfx950).
+//
+// foundry "PagedAttention" ops page, "How it works": each decode step stores
+// the new token's key and value into the sequence's current block; shared
+// blocks are duplicated (copy-on-write) when a sharer writes.  "At a glance":
+// a block is copied only when a sequence writes to it.
+//
+// Both kernels move bytes only (16 bytes per lane, coalesced) and are
+// bitwise exact.  Pool layout: [num_blocks][num_kv_heads][block_size][head_dim].
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_status.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// One lane moves 16 bytes of one token row of one KV head, for K and V.
+// Rows are head_dim * elt bytes, a multiple of 16.
+__global__ __launch_bounds__(kThreads) void write_kv_kernel(
+    const uint4 *__restrict__ k, const uint4 *__restrict__ v, const int64_t *__restrict__ slots,
+    int64_t num_chunks, int32_t chunks_per_row, int32_t num_kv_heads, int32_t block_size,
+    int64_t num_slots, uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache) {
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= num_chunks) return;
+  int64_t row = i / chunks_per_row;          // token * num_kv_heads + head
+  int32_t c = (int32_t)(i - row * chunks_per_row);
+  int64_t tok = row / num_kv_heads;
+  int32_t head = (int32_t)(row - tok * num_kv_heads);
+  int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;  // padding / out of pool: skipped
+  int64_t blk = slot / block_size;
+  int64_t off = slot - blk * block_size;
+  int64_t dst = ((blk * num_kv_heads + head) * block_size + off) * chunks_per_row + c;
+  k_cache[dst] = k[i];
+  v_cache[dst] = v[i];
+}
+
+// Workgroup w copies part (w % parts) of pair (w / parts); a block's bytes
+// are split over `parts` workgroups of kThreads lanes.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, const int64_t *__restrict__ pairs,
+    int64_t chunks_per_block, int32_t parts, int32_t num_blocks) {
+  int64_t pair = blockIdx.x / parts;
+  int32_t part = (int32_t)(blockIdx.x - pair * parts);
+  int64_t src = pairs[2 * pair];
+  int64_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4 *ks = k_cache + src * chunks_per_block;
+  const uint4 *vs = v_cache + src * chunks_per_block;
+  uint4 *kd = k_cache + dst * chunks_per_block;
+  uint4 *vd = v_cache + dst * chunks_per_block;
+  for (int64_t i = (int64_t)part * kThreads + threadIdx.x; i < chunks_per_block;
+       i += (int64_t)parts * kThreads) {
+    uint4 a = ks[i];
+    uint4 b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+int elt_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : dtype == PA_F32 ? 4 : 0; }
+
+pa_status_t check_cache(const char *who, const pa_cache_t *c) {
+  if (!c) return pa::fail(PA_EINVAL, "%s: cache descriptor is NULL", who);
+  if (c->num_blocks <= 0 || c->block_size <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+    return pa::fail(PA_EINVAL, "%s: cache dimensions must be > 0", who);
+  if (!elt_bytes(c->dtype)) return pa::fail(PA_EUNSUPPORTED, "%s: dtype %d", who, c->dtype);
+  if ((c->head_dim * elt_bytes(c->dtype)) % 16)
+    return pa::fail(PA_EUNSUPPORTED, "%s: a row of head_dim %d is not a multiple of 16 bytes", who,
+                    c->head_dim);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_write_kv(const void *k, const void *v, const int64_t *slot_mapping,
+                                   int32_t num_tokens, void *k_cache, void *v_cache,
+                                   const pa_cache_t *cache, void *stream) {
+  if (pa_status_t st = check_cache("pa_write_kv", cache)) return st;
+  if (num_tokens < 0) return pa::fail(PA_EINVAL, "pa_write_kv: num_tokens=%d < 0", num_tokens);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return pa::fail(PA_EINVAL, "pa_write_kv: NULL pointer");
+  int32_t cpr = cache->head_dim * elt_bytes(cache->dtype) / 16;
+  int64_t chunks = (int64_t)num_tokens * cache->num_kv_heads * cpr;
+  int64_t grid = (chunks + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const uint4 *)k, (const uint4 *)v, slot_mapping, chunks, cpr,
+                     cache->num_kv_heads, cache->block_size,
+                     (int64_t)cache->num_blocks * cache->block_size, (uint4 *)k_cache,
+                     (uint4 *)v_cache);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_EHIP, "pa_write_kv: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+extern "C" pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cache_t *cache,
+                                      const int64_t *src_dst_pairs, int32_t num_pairs,
+                                      void *stream) {
+  if (pa_status_t st = check_cache("pa_copy_blocks", cache)) return st;
+  if (num_pairs < 0) return pa::fail(PA_EINVAL, "pa_copy_blocks: num_pairs=%d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs) return pa::fail(PA_EINVAL, "pa_copy_blocks: NULL pointer");
+  int64_t block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim *
+                        elt_bytes(cache->dtype);
+  int64_t chunks = block_bytes / 16;
+  int64_t parts = (chunks + kThreads - 1) / kThreads;
+  if (parts > 64) parts = 64;
+  int64_t grid = parts * num_pairs;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint4 *)k_cache, (uint4 *)v_cache, src_dst_pairs, chunks,
+                     (int32_t)parts, cache->num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return pa::fail(PA_EHIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

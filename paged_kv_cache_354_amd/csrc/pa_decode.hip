@@ -1,0 +1,560 @@
+// Paged single-query decode attention for gfx950 (MI355X).
+//
+// foundry "PagedAttention" ops page, "How it works": the attention kernel
+// reads KV through the per-sequence block table, gathering scattered
+// physical blocks, so the math is the same as over one contiguous run;
+// "Concept": blocks hold a fixed number of tokens and live anywhere in the
+// pool.  The math is softmax(scale * q K^T) V per (sequence, query head),
+// accumulated in fp32 with an online softmax (Milakov & Gimelshein 2018).
+//
+// Work decomposition
+//   One workgroup of 4 wave64s per (sequence, KV head, context partition).
+//   The G = Hq / Hkv query heads of a KV head share that workgroup, so each
+//   K/V row is read from HBM once.  A K or V row is head_dim elements; a lane
+//   owns 16 bytes of it, so LPR = row_bytes / 16 lanes cover a row and one
+//   wave-wide load streams RPW = 64 / LPR consecutive rows (1 KiB).  Lane
+//   (r, c) = (lane / LPR, lane % LPR) holds channels [c*VEC, c*VEC + VEC) of
+//   row r of each load.
+//   The block-table slice of the workgroup's tokens is staged in LDS first;
+//   each token's row address is then pool + ((blk * Hkv + kvh) * bs + off) * row.
+//   QK: per-lane partial dots, summed over the LPR lanes of a row with DPP
+//   row permutations (every lane ends with the identical sum).  Softmax runs
+//   in the exp2 domain (logits pre-multiplied by log2 e); each row group keeps
+//   its own running (max, sum, acc) and the groups / waves are merged at the
+//   end (shuffles, then LDS).
+//   Partitioned mode writes per-partition (max, sum, unnormalised acc) to the
+//   workspace and a second kernel merges them:
+//     M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+//
+// Masking: tokens at or past the sequence length are never loaded and their
+// logits are -inf (selected, not multiplied), so whatever the tail slots of
+// the last block hold cannot reach the output.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_status.h"
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerTile = 4;             // 16-byte loads per lane per K (and V) tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;          // running-max start; finite keeps exp2 defined
+constexpr int kMaxTableLds = 4096;           // staged block ids per workgroup (16 KiB)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct DecodeArgs {
+  const uint4 *q;
+  const uint4 *k_cache;
+  const uint4 *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  void *out;
+  float *part_m;   // [B][Hq][NP]
+  float *part_l;   // [B][Hq][NP]
+  float *part_o;   // [B][Hq][NP][D]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t log2_bs;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t partition_size;  // tokens per partition (unpartitioned: >= every length)
+  int32_t num_parts;       // partitions per (sequence, KV head) in the grid
+  int32_t ctx_cap;         // lengths are clamped to this
+  int32_t out_f32;         // 1: fp32 output, 0: cache element type
+  float qscale;            // scale * log2(e)
+};
+
+template <typename E>
+struct Elt;
+template <>
+struct Elt<float> {
+  static constexpr int kVec = 4;   // elements per 16 bytes
+};
+template <>
+struct Elt<uint16_t> {
+  static constexpr int kVec = 8;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 pattern, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPR lanes; every lane of a group gets the same
+// value (each step adds a partner's value; a + b == b + a exactly).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (LPR >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
+  if constexpr (LPR >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
+  if constexpr (LPR >= 8) x = dpp_add<0x141>(x);   // row_half_mirror: other quad of the 8
+  if constexpr (LPR >= 16) x = dpp_add<0x140>(x);  // row_mirror: other half of the 16
+  if constexpr (LPR >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (LPR >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup L runs on
+// XCD L % 8).  Renumber so that every XCD receives one contiguous range of
+// work ids: neighbouring work (same KV head, same partition) shares an L2.
+__device__ __forceinline__ int xcd_work_id(int L, int N) {
+  int xcd = L & 7, idx = L >> 3;
+  int q = N >> 3, r = N & 7;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+// Lane-owned query chunk for G heads, in the form the dot product wants.
+template <typename E, int G>
+struct QChunk;
+
+template <int G>
+struct QChunk<float, G> {
+  float v[G][4];
+  __device__ __forceinline__ void load(const uint4 *q, int stride_heads_chunks, float qscale) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      uint4 w = q[j * stride_heads_chunks];
+      v[j][0] = __uint_as_float(w.x) * qscale;
+      v[j][1] = __uint_as_float(w.y) * qscale;
+      v[j][2] = __uint_as_float(w.z) * qscale;
+      v[j][3] = __uint_as_float(w.w) * qscale;
+    }
+  }
+  // Partial dot of head j with one lane chunk of a K row, already scaled.
+  __device__ __forceinline__ float dot(int j, uint4 k) const {
+    float s = v[j][0] * __uint_as_float(k.x);
+    s = fmaf(v[j][1], __uint_as_float(k.y), s);
+    s = fmaf(v[j][2], __uint_as_float(k.z), s);
+    s = fmaf(v[j][3], __uint_as_float(k.w), s);
+    return s;
+  }
+  static constexpr bool kPostScale = false;
+};
+
+template <int G>
+struct QChunk<uint16_t, G> {
+  uint4 v[G];
+  __device__ __forceinline__ void load(const uint4 *q, int stride_heads_chunks, float) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) v[j] = q[j * stride_heads_chunks];
+  }
+  // bf16 pairs: v_dot2_f32_bf16 accumulates both products into fp32.
+  __device__ __forceinline__ float dot(int j, uint4 k) const {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
+                                              __builtin_bit_cast(bf16x2_t, v[j].x), 0.0f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
+                                        __builtin_bit_cast(bf16x2_t, v[j].y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
+                                        __builtin_bit_cast(bf16x2_t, v[j].z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
+                                        __builtin_bit_cast(bf16x2_t, v[j].w), s, false);
+    return s;
+  }
+  static constexpr bool kPostScale = true;
+};
+
+template <typename E>
+__device__ __forceinline__ void widen(uint4 w, float (&f)[Elt<E>::kVec]);
+
+template <>
+__device__ __forceinline__ void widen<float>(uint4 w, float (&f)[4]) {
+  f[0] = __uint_as_float(w.x);
+  f[1] = __uint_as_float(w.y);
+  f[2] = __uint_as_float(w.z);
+  f[3] = __uint_as_float(w.w);
+}
+
+template <>
+__device__ __forceinline__ void widen<uint16_t>(uint4 w, float (&f)[8]) {
+  f[0] = bf16_lo(w.x);
+  f[1] = bf16_hi(w.x);
+  f[2] = bf16_lo(w.y);
+  f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z);
+  f[5] = bf16_hi(w.z);
+  f[6] = bf16_lo(w.w);
+  f[7] = bf16_hi(w.w);
+}
+
+template <typename E>
+__device__ __forceinline__ void store_out(void *out, size_t idx, float x, int out_f32) {
+  if (out_f32 || sizeof(E) == 4)
+    static_cast<float *>(out)[idx] = x;
+  else
+    static_cast<uint16_t *>(out)[idx] = to_bf16(x);
+}
+
+template <typename E, int D, int G, bool PART>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  constexpr int VEC = Elt<E>::kVec;
+  constexpr int LPR = D / VEC;        // lanes per row
+  constexpr int RPW = 64 / LPR;       // rows per wave-wide load
+  constexpr int U = kLoadsPerTile;
+  constexpr int TILE = RPW * U;       // tokens per wave iteration
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "row must map onto a wave");
+
+  extern __shared__ int32_t tbl[];
+  __shared__ float red_m[kWaves][G];
+  __shared__ float red_l[kWaves][G];
+  __shared__ float red_acc[kWaves][G][D];
+
+  const int n_work = a.num_seqs * a.num_kv_heads * a.num_parts;
+  const int w = xcd_work_id(blockIdx.x, n_work);
+  // work order: KV head (slowest), partition, sequence (fastest)
+  const int s = w % a.num_seqs;
+  const int rest = w / a.num_seqs;
+  const int p = rest % a.num_parts;
+  const int kvh = rest / a.num_parts;
+
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  const int start = p * a.partition_size;
+  const int end = min(ctx, start + a.partition_size);
+  if (PART && start >= end) return;  // no tokens: the merge never reads this slot
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane / LPR;
+  const int c = lane % LPR;
+  const int bs = a.block_size;
+  const int first_blk = start >> a.log2_bs;
+  const int nblk = end > start ? ((end - 1) >> a.log2_bs) - first_blk + 1 : 0;
+
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks + first_blk;
+  for (int i = tid; i < nblk; i += kThreads) {
+    int b = trow[i];
+    tbl[i] = (unsigned)b < (unsigned)a.num_blocks ? b : 0;  // stay inside the pool
+  }
+
+  QChunk<E, G> qc;
+  const int h0 = kvh * G;
+  qc.load(a.q + ((size_t)s * a.num_q_heads + h0) * LPR + c, LPR, a.qscale);
+
+  float m[G], l[G], acc[G][VEC];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = kNegBig;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[j][e] = 0.0f;
+  }
+  __syncthreads();
+
+  const size_t head_rows = (size_t)kvh * bs;        // row offset of this head in a block
+  const size_t block_rows = (size_t)a.num_kv_heads * bs;
+  const uint4 *kbase = a.k_cache + c;
+  const uint4 *vbase = a.v_cache + c;
+
+  for (int t0 = start + wave * TILE; t0 < end; t0 += kWaves * TILE) {
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * RPW + r;
+      if (t < end) {
+        const int blk = tbl[(t >> a.log2_bs) - first_blk];
+        const size_t row = (size_t)blk * block_rows + head_rows + (t & (bs - 1));
+        kr[u] = kbase[row * LPR];
+        vr[u] = vbase[row * LPR];
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float z[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool valid = t0 + u * RPW + r < end;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float d = group_sum<LPR>(qc.dot(j, kr[u]));
+        if (QChunk<E, G>::kPostScale) d *= a.qscale;
+        z[u][j] = valid ? d : -INFINITY;
+      }
+    }
+    float vf[U][VEC];
+#pragma unroll
+    for (int u = 0; u < U; ++u) widen<E>(vr[u], vf[u]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float mt = z[0][j];
+#pragma unroll
+      for (int u = 1; u < U; ++u) mt = fmaxf(mt, z[u][j]);
+      const float mn = fmaxf(m[j], mt);
+      const float alpha = exp2_fast(m[j] - mn);
+      m[j] = mn;
+      l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pr = exp2_fast(z[u][j] - mn);
+        l[j] += pr;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[j][e] = fmaf(pr, vf[u][e], acc[j][e]);
+      }
+    }
+  }
+
+  // Merge the RPW row groups of the wave (lanes c, c + LPR, c + 2 LPR, ...).
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mo = __shfl_xor(m[j], off, 64);
+      const float lo = __shfl_xor(l[j], off, 64);
+      const float mn = fmaxf(m[j], mo);
+      const float a1 = exp2_fast(m[j] - mn);
+      const float a2 = exp2_fast(mo - mn);
+      l[j] = l[j] * a1 + lo * a2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float ao = __shfl_xor(acc[j][e], off, 64);
+        acc[j][e] = acc[j][e] * a1 + ao * a2;
+      }
+      m[j] = mn;
+    }
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red_acc[wave][j][c * VEC + e] = acc[j][e];
+      if (c == 0) {
+        red_m[wave][j] = m[j];
+        red_l[wave][j] = l[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves: one output element per thread step.
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int j = idx / D;
+    const int ch = idx % D;
+    float M = red_m[0][j];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) M = fmaxf(M, red_m[wv][j]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const float f = exp2_fast(red_m[wv][j] - M);
+      L = fmaf(red_l[wv][j], f, L);
+      A = fmaf(red_acc[wv][j][ch], f, A);
+    }
+    const int h = h0 + j;
+    if (PART) {
+      const size_t slot = ((size_t)s * a.num_q_heads + h) * a.num_parts + p;
+      a.part_o[slot * D + ch] = A;
+      if (ch == 0) {
+        a.part_m[slot] = M;
+        a.part_l[slot] = L;
+      }
+    } else {
+      const float o = L > 0.0f ? A / L : 0.0f;
+      store_out<E>(a.out, ((size_t)s * a.num_q_heads + h) * D + ch, o, a.out_f32);
+    }
+  }
+}
+
+// Merge of partition statistics: one workgroup of D threads per (seq, q head).
+template <typename E, int D>
+__global__ __launch_bounds__(D) void merge_kernel(DecodeArgs a) {
+  const int s = blockIdx.x / a.num_q_heads;
+  const int h = blockIdx.x % a.num_q_heads;
+  const int ch = threadIdx.x;
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  int np = (ctx + a.partition_size - 1) / a.partition_size;
+  np = np > a.num_parts ? a.num_parts : np;
+  const size_t base = ((size_t)s * a.num_q_heads + h) * a.num_parts;
+  float M = kNegBig;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[base + p]);
+  float L = 0.0f, A = 0.0f;
+  for (int p = 0; p < np; ++p) {
+    const float f = exp2_fast(a.part_m[base + p] - M);
+    L = fmaf(a.part_l[base + p], f, L);
+    A = fmaf(a.part_o[(base + p) * D + ch], f, A);
+  }
+  const float o = L > 0.0f ? A / L : 0.0f;
+  store_out<E>(a.out, ((size_t)s * a.num_q_heads + h) * D + ch, o, a.out_f32);
+}
+
+template <typename E, int D, int G>
+hipError_t launch(const DecodeArgs &a, bool part, int nblk_lds, hipStream_t st) {
+  const int n_work = a.num_seqs * a.num_kv_heads * a.num_parts;
+  const size_t lds = (size_t)nblk_lds * sizeof(int32_t);
+  if (part) {
+    hipLaunchKernelGGL((decode_kernel<E, D, G, true>), dim3(n_work), dim3(kThreads), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<E, D, G, false>), dim3(n_work), dim3(kThreads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_g(int g, const DecodeArgs &a, bool part, int nblk_lds, hipStream_t st) {
+  switch (g) {
+    case 1: return launch<E, D, 1>(a, part, nblk_lds, st);
+    case 2: return launch<E, D, 2>(a, part, nblk_lds, st);
+    case 4: return launch<E, D, 4>(a, part, nblk_lds, st);
+    case 8: return launch<E, D, 8>(a, part, nblk_lds, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_d(int d, int g, const DecodeArgs &a, bool part, int nblk_lds, hipStream_t st) {
+  switch (d) {
+    case 64: return launch_g<E, 64>(g, a, part, nblk_lds, st);
+    case 128: return launch_g<E, 128>(g, a, part, nblk_lds, st);
+    case 256: return launch_g<E, 256>(g, a, part, nblk_lds, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WorkspaceLayout {
+  size_t m_off, l_off, o_off, total;
+};
+
+WorkspaceLayout layout(int64_t b, int64_t hq, int64_t d, int64_t np) {
+  WorkspaceLayout w;
+  size_t ml = align256((size_t)(b * hq * np) * sizeof(float));
+  w.m_off = 0;
+  w.l_off = ml;
+  w.o_off = 2 * ml;
+  w.total = 2 * ml + align256((size_t)(b * hq * np * d) * sizeof(float));
+  return w;
+}
+
+int64_t parts_for(int64_t max_ctx, int64_t part) {
+  int64_t np = (max_ctx + part - 1) / part;
+  return np < 1 ? 1 : np;
+}
+
+}  // namespace
+
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                            int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  int64_t mc = max_context_len < 0 ? 0 : max_context_len;
+  return layout(num_seqs, num_q_heads, head_dim, parts_for(mc, partition_size)).total;
+}
+
+extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
+                                 const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, int32_t max_context_len, float scale,
+                                 int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                 void *out, int32_t out_dtype, void *stream) {
+  using pa::fail;
+  if (!cache) return fail(PA_EINVAL, "pa_decode: cache descriptor is NULL");
+  const pa_cache_t c = *cache;
+  if (num_seqs < 0 || num_q_heads <= 0 || c.num_blocks <= 0 || c.num_kv_heads <= 0 ||
+      c.block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return fail(PA_EINVAL, "pa_decode: sizes must be positive (num_seqs may be 0)");
+  if (c.dtype != PA_F32 && c.dtype != PA_BF16)
+    return fail(PA_EUNSUPPORTED, "pa_decode: cache dtype %d", c.dtype);
+  if (out_dtype != PA_F32 && out_dtype != c.dtype)
+    return fail(PA_EUNSUPPORTED, "pa_decode: out dtype %d (use PA_F32 or the cache dtype)", out_dtype);
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)
+    return fail(PA_EUNSUPPORTED, "pa_decode: head_dim %d (built: 64, 128, 256)", c.head_dim);
+  if (c.block_size > 256 || (c.block_size & (c.block_size - 1)))
+    return fail(PA_EUNSUPPORTED, "pa_decode: block_size %d (powers of two up to 256)", c.block_size);
+  if (num_q_heads % c.num_kv_heads)
+    return fail(PA_EINVAL, "pa_decode: %d query heads not a multiple of %d KV heads", num_q_heads,
+                c.num_kv_heads);
+  const int g = num_q_heads / c.num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_EUNSUPPORTED, "pa_decode: query heads per KV head = %d (built: 1, 2, 4, 8)", g);
+  if (partition_size < 0 || (partition_size % c.block_size))
+    return fail(PA_EINVAL, "pa_decode: partition_size %d must be 0 or a multiple of block_size %d",
+                partition_size, c.block_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PA_EINVAL, "pa_decode: NULL pointer");
+
+  int log2_bs = 0;
+  while ((1 << log2_bs) < c.block_size) ++log2_bs;
+  const int64_t cap64 = (int64_t)max_blocks_per_seq * c.block_size;
+  const int32_t ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
+  const bool part = partition_size > 0;
+
+  DecodeArgs a{};
+  a.q = (const uint4 *)q;
+  a.k_cache = (const uint4 *)k_cache;
+  a.v_cache = (const uint4 *)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c.num_kv_heads;
+  a.block_size = c.block_size;
+  a.log2_bs = log2_bs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = c.num_blocks;
+  a.ctx_cap = ctx_cap;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  a.qscale = scale * kLog2e;
+
+  int nblk_lds;
+  if (part) {
+    const int64_t np = parts_for(ctx_cap, partition_size);
+    const WorkspaceLayout wl = layout(num_seqs, num_q_heads, c.head_dim, np);
+    if (!workspace || workspace_bytes < wl.total)
+      return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes < %zu needed", workspace_bytes,
+                  wl.total);
+    if ((uintptr_t)workspace % 16)
+      return fail(PA_EINVAL, "pa_decode: workspace must be 16-byte aligned");
+    a.partition_size = partition_size;
+    a.num_parts = (int32_t)np;
+    a.part_m = (float *)((char *)workspace + wl.m_off);
+    a.part_l = (float *)((char *)workspace + wl.l_off);
+    a.part_o = (float *)((char *)workspace + wl.o_off);
+    nblk_lds = partition_size / c.block_size;
+  } else {
+    a.partition_size = ctx_cap > 0 ? ctx_cap : 1;
+    a.num_parts = 1;
+    nblk_lds = (ctx_cap + c.block_size - 1) / c.block_size;
+  }
+  if (nblk_lds > kMaxTableLds)
+    return fail(PA_EUNSUPPORTED,
+                "pa_decode: %d blocks per workgroup exceed %d; use a smaller partition_size",
+                nblk_lds, kMaxTableLds);
+  const int64_t n_work = (int64_t)num_seqs * c.num_kv_heads * a.num_parts;
+  if (n_work > 0x7fffffff) return fail(PA_EINVAL, "pa_decode: grid of %lld workgroups too large", (long long)n_work);
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
+    return fail(PA_EINVAL, "pa_decode: q and the pools must be 16-byte aligned");
+
+  hipError_t e = c.dtype == PA_F32
+                     ? launch_d<float>(c.head_dim, g, a, part, nblk_lds, (hipStream_t)stream)
+                     : launch_d<uint16_t>(c.head_dim, g, a, part, nblk_lds, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

@@ -1,0 +1,50 @@
+"""The C ABI library loads and exports every entry point its header declares (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_354_amd as pkv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_hot_path_calls():
+    names = declared()
+    for n in ("pa_write_kv", "pa_decode", "pa_copy_blocks", "pa_decode_workspace_bytes",
+              "pa_pool_create", "pa_seq_append", "pa_seq_cow", "pa_seq_free"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_binding_covers_every_declared_symbol():
+    assert sorted(pkv.EXPORTED) == declared()
+
+
+def test_version_and_error_strings():
+    assert "gfx950" in pkv.pa_version()
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.BlockPool(-1, 4)
+    assert "num_blocks" in str(e.value)
+
+
+def test_workspace_bytes_host_only():
+    # partitioned: [B][Hq][NP] max + sum, [B][Hq][NP][d] accumulators, 256-byte aligned
+    n = pkv.pa_decode_workspace_bytes(8, 32, 128, 32768, 512)
+    np_ = 64
+    ml = -(-(8 * 32 * np_ * 4) // 256) * 256
+    assert n == 2 * ml + -(-(8 * 32 * np_ * 128 * 4) // 256) * 256
+    assert pkv.pa_decode_workspace_bytes(8, 32, 128, 32768, 0) == 0

@@ -1,0 +1,214 @@
+"""pa_decode on the GPU against the fp64 oracle.
+
+Tolerances (stated by the workload definition): fp32 KV -> max abs 1e-4;
+bf16 KV with fp32 accumulation and bf16 output -> |err| <= 2e-2 + 1e-2|ref|.
+Stricter diagnostics: every bf16 case also runs with an fp32 output, where
+the only error left is fp32 accumulation order and exp2, held to 1e-4 abs;
+and a needle test that pins gathering, tails and lengths exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as A
+
+from gpu_cases import (DevCase, announce, check_decode, oracle_after_write, out_to_f64,
+                       small_bf16_case, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(pkv, case, partitions, f32_out_too=True):
+    dc = DevCase(case)
+    dc.write(pkv)
+    kc, vc = oracle_after_write(case)
+    ref = A.decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
+    errs = {}
+    for p in partitions:
+        outs = [None] if case.dtype == W.F32 else ([None, torch.float32] if f32_out_too else [None])
+        for od in outs:
+            announce(case.name, "P", p, "out", od)
+            got = out_to_f64(dc.decode(pkv, partition_size=p, out_dtype=od))
+            bf16_out = case.dtype == W.BF16 and od is None
+            errs[(p, od)] = check_decode(got, ref, bf16_out)
+    return errs
+
+
+@pytest.mark.parametrize("seed", [1, 101, 102, 103])
+def test_tiny_f32(gpu_lib, seed):
+    case = W.c1_tiny_f32(seed=seed)
+    run_and_check(gpu_lib, case, [0, 16, 32, 48, 112])
+
+
+@pytest.mark.parametrize("seed", [2, 101, 102])
+def test_small_bf16_gqa4(gpu_lib, seed):
+    case = small_bf16_case(seed)
+    run_and_check(gpu_lib, case, [0, 16, 64, 512])
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs", [
+    (W.BF16, 8, 8, 128, 8), (W.BF16, 8, 4, 128, 32), (W.BF16, 16, 2, 128, 16),
+    (W.BF16, 4, 4, 64, 16), (W.BF16, 8, 2, 256, 16), (W.BF16, 4, 4, 128, 1),
+    (W.BF16, 8, 4, 128, 2), (W.BF16, 4, 1, 64, 4), (W.F32, 8, 2, 64, 8), (W.F32, 4, 4, 128, 16),
+    (W.F32, 2, 1, 256, 32), (W.BF16, 8, 1, 128, 64), (W.BF16, 2, 2, 128, 256)])
+def test_shape_grid(gpu_lib, dtype, hq, hkv, d, bs):
+    rng = np.random.default_rng(hq * 7 + d + bs)
+    lens = [1, bs, bs + 1, 2 * bs - 1] + list(rng.integers(1, 400, size=4))
+    case = W.make_case(f"grid_{dtype}_{hq}_{hkv}_{d}_{bs}", seed=int(rng.integers(1 << 30)), dtype=dtype,
+                       context_lens=lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs)
+    parts = [0, bs * max(1, 64 // bs), 256 if bs <= 256 else bs]
+    run_and_check(gpu_lib, case, sorted(set(parts)))
+
+
+def test_poisoned_tails_unused_blocks_and_write_slot(gpu_lib):
+    case = small_bf16_case(7, poison=True)
+    run_and_check(gpu_lib, case, [0, 16, 128])
+    f32case = W.c1_tiny_f32(seed=9, poison=True)
+    run_and_check(gpu_lib, f32case, [0, 16])
+
+
+def test_table_padding_is_never_read(gpu_lib):
+    # -1 padding plus extra columns beyond every sequence's blocks
+    case = small_bf16_case(8, max_blocks=80)
+    assert (case.block_tables[:, -1] == -1).all()
+    run_and_check(gpu_lib, case, [0, 32])
+
+
+def test_zero_and_one_token_sequences(gpu_lib):
+    announce("ctx 0/1")
+    case = W.make_case("ctx01", seed=3, dtype=W.BF16, context_lens=[0, 1, 5, 0, 1],
+                       num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16)
+    dc = DevCase(case)
+    for p in (0, 16):
+        out = dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy()
+        assert not out[0].any() and not out[3].any()
+        from oracle.numerics import to_f64
+        v = to_f64(case.v_cache, W.BF16)  # a 1-token softmax returns that token's V row exactly
+        for s in (1, 4):
+            blk = case.block_tables[s, 0]
+            for h in range(8):
+                assert np.array_equal(out[s, h].astype(np.float64), v[blk, h // 4, 0])
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_needle_coverage(gpu_lib, dtype):
+    """q = 0 gives p = 1/ctx exactly; one-hot V probes every block, the first and
+    last token and the tail, so a missed / duplicated / foreign token shows up
+    as an error >= 1/ctx."""
+    announce("needle", dtype)
+    bs, d, hkv = 16, 128 if dtype == W.BF16 else 64, 2
+    lens = [1, 17, 100, 257, 1000, 2049]
+    case = W.make_case("needle", seed=5, dtype=dtype, context_lens=lens, num_q_heads=4,
+                       num_kv_heads=hkv, head_dim=d, block_size=bs, poison=True)
+    one = np.uint16(0x3F80) if dtype == W.BF16 else np.float32(1)
+    zero = np.uint16(0) if dtype == W.BF16 else np.float32(0)
+    case.q[...] = zero
+    expect = np.zeros((len(lens), 4, d))
+    vc = case.v_cache
+    for s, n in enumerate(lens):
+        nb = W.ceil_div(n, bs)
+        for t in range(n):  # zero all valid rows (poison stays past the ends)
+            vc[case.block_tables[s, t // bs], :, t % bs, :] = zero
+        probes = sorted(set([0, n - 1] + [b * bs + (b * 5) % bs for b in range(nb)]))
+        probes = [t for t in probes if t < n][:d]
+        for j, t in enumerate(probes):
+            for g in range(hkv):
+                vc[case.block_tables[s, t // bs], g, t % bs, (j + g) % d] = one
+                expect[s, 2 * g:2 * g + 2, (j + g) % d] = 1.0 / n
+    # the write puts the new token (position n - 1) back: make it zero except its probe
+    case.k_new[...] = zero
+    case.v_new[...] = zero
+    for s, n in enumerate(lens):
+        blk, off = divmod(int(case.slot_mapping[s]), bs)
+        case.v_new[s] = vc[blk, :, off, :]
+    dc = DevCase(case)
+    dc.write(gpu_lib)
+    for p in (0, 16, 512):
+        got = dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+        np.testing.assert_allclose(got, expect, rtol=1e-5, atol=1e-7)
+
+
+def test_placement_permutation_is_bitwise_invariant(gpu_lib):
+    announce("placement invariance")
+    a = small_bf16_case(31)
+    b = small_bf16_case(31)
+    rng = np.random.default_rng(3)
+    newpos = rng.permutation(a.num_blocks)
+    b.k_cache = np.empty_like(a.k_cache)
+    b.v_cache = np.empty_like(a.v_cache)
+    b.k_cache[newpos] = a.k_cache
+    b.v_cache[newpos] = a.v_cache
+    b.block_tables = np.where(a.block_tables >= 0, newpos[np.maximum(a.block_tables, 0)], -1).astype(np.int32)
+    b.slot_mapping = np.array([newpos[s // a.block_size] * a.block_size + s % a.block_size
+                               for s in a.slot_mapping], np.int64)
+    da, db = DevCase(a), DevCase(b)
+    da.write(gpu_lib)
+    db.write(gpu_lib)
+    for p in (0, 64):
+        oa = da.decode(gpu_lib, partition_size=p, out_dtype=torch.float32)
+        ob = db.decode(gpu_lib, partition_size=p, out_dtype=torch.float32)
+        assert torch.equal(oa, ob)
+
+
+def test_partition_sizes_agree(gpu_lib):
+    announce("partition agreement")
+    case = small_bf16_case(41, hi=3000)
+    dc = DevCase(case)
+    outs = [dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy()
+            for p in (0, 16, 64, 256, 1024)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 2e-6
+
+
+def test_argument_errors(gpu_lib):
+    announce("argument errors")
+    case = small_bf16_case(51, num_seqs=2)
+    dc = DevCase(case)
+    with pytest.raises(gpu_lib.PagedKVError):
+        dc.decode(gpu_lib, partition_size=24)  # not a multiple of the block size
+    with pytest.raises(gpu_lib.PagedKVError):
+        gpu_lib.pa_decode(dc.q[:, :12].contiguous(), dc.k_cache, dc.v_cache, dc.block_tables,
+                          dc.context_lens, case.max_context, case.scale)  # 12 / 8 heads
+    with pytest.raises(ValueError):
+        gpu_lib.pa_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables[:1], dc.context_lens,
+                          case.max_context, case.scale)
+
+
+# --- full-size workloads, checked on sampled rows ----------------------------------
+
+@pytest.mark.parametrize("name,partition", [("llama3_8b_b64", 0), ("llama3_8b_b64", 512),
+                                            ("long_ctx_32k", 512), ("mha_b256_bs8", 0),
+                                            ("mha_b256_bs16", 0), ("mha_b256_bs32", 0),
+                                            ("mha_b256_bs16", 256)])
+def test_full_size_sampled(gpu_lib, name, partition):
+    announce("full", name, "P", partition)
+    if name == "llama3_8b_b64":
+        case = W.c2_llama8b_b64()
+    elif name == "long_ctx_32k":
+        case = W.c3_long_context()
+    else:
+        case = W.c5_mha_sweep(block_size=int(name.split("bs")[1]))
+    dc = DevCase(case)
+    dc.write(gpu_lib)
+    out32 = dc.decode(gpu_lib, partition_size=partition, out_dtype=torch.float32)
+    outbf = dc.decode(gpu_lib, partition_size=partition)
+    got32 = out32.cpu().numpy().astype(np.float64)
+    gotbf = out_to_f64(outbf)
+    assert np.isfinite(got32).all() and np.isfinite(gotbf).all()
+    # bf16 output is the fp32 output rounded once
+    assert np.max(np.abs(gotbf - got32)) <= np.max(np.abs(got32)) * 2 ** -8
+    rng = np.random.default_rng(7)
+    kc, vc = oracle_after_write(case)
+    grp = case.num_q_heads // case.num_kv_heads
+    rows = {(int(s), int(h)) for s, h in zip(rng.integers(0, case.num_seqs, 48),
+                                             rng.integers(0, case.num_q_heads, 48))}
+    rows |= {(int(np.argmax(case.context_lens)), 0), (int(np.argmin(case.context_lens)), case.num_q_heads - 1)}
+    for s, h in sorted(rows):
+        ref = A.decode_one(case.q[s, h], kc, vc, case.block_tables[s], case.context_lens[s], case.scale,
+                           case.dtype, h // grp)
+        check_decode(got32[s, h], ref, bf16_out=False)
+        check_decode(gotbf[s, h], ref, bf16_out=True)
+    del dc, out32, outbf
+    torch.cuda.empty_cache()

@@ -17,11 +17,15 @@ Layouts (the library's ABI):
 
 Recipe (one ``numpy.random.default_rng(seed)`` PCG64 stream, drawn in this
 order): context lengths, block placement permutation, q, K pool, V pool, new
-K rows, new V rows.  Values are N(0, 1).  The pool holds
+K rows, new V rows.  Values are N(0, 1); arrays above 2**24 elements are
+drawn chunk by chunk from PCG64 streams seeded from the main stream (see
+``normal``).  The pool holds
 ceil(1.25 * blocks in use) blocks unless a size is given; the blocks in use are
 the first entries of the permutation, handed to sequences in order.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -52,14 +56,31 @@ def storage_dtype(dtype):
     return np.uint16 if dtype == BF16 else np.float32
 
 
+def _fill_chunk(seed, out, dtype):
+    x = np.random.default_rng(seed).standard_normal(out.size, dtype=np.float32)
+    out[...] = x if dtype == F32 else round_to_bf16(x)
+
+
 def normal(rng, shape, dtype):
-    """N(0, 1) draws of ``shape`` stored as ``dtype``; drawn in chunks."""
+    """N(0, 1) draws of ``shape`` stored as ``dtype``.
+
+    Small arrays come straight from ``rng``.  Large ones are cut into fixed
+    chunks of 2**24 elements; chunk i is drawn from a PCG64 seeded with the
+    i-th of a list of 63-bit integers taken from ``rng``, so the values do
+    not depend on how many threads fill the chunks.
+    """
     out = np.empty(shape, dtype=storage_dtype(dtype))
     flat = out.reshape(-1)
-    for i in range(0, flat.size, _CHUNK):
-        n = min(_CHUNK, flat.size - i)
-        x = rng.standard_normal(n, dtype=np.float32)
-        flat[i:i + n] = x if dtype == F32 else round_to_bf16(x)
+    if flat.size <= _CHUNK:
+        x = rng.standard_normal(flat.size, dtype=np.float32)
+        flat[:] = x if dtype == F32 else round_to_bf16(x)
+        return out
+    n = -(-flat.size // _CHUNK)
+    seeds = rng.integers(0, 2 ** 63 - 1, size=n)
+    workers = max(1, min(16, os.cpu_count() or 1, n))
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda i: _fill_chunk(int(seeds[i]), flat[i * _CHUNK:(i + 1) * _CHUNK], dtype),
+                    range(n)))
     return out
 
 
