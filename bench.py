@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X (gfx950).
+
+One *step* is one decode step of a batch, as a serving loop runs it:
+
+  a1  host block manager: reserve each sequence's slot for its new token,
+      extend block tables from the free pool, emit copy-on-write pairs
+      (done for every step before the timed region; its host time is
+      reported separately as ``host_prep_us``)
+  a2  pa_copy_blocks  (only when the step has copy-on-write pairs)
+  a3  pa_write_kv     (one new token per sequence)
+  a4  pa_decode       (K1, plus the partition-merge kernel K1b when
+      partition_size > 0)
+
+Each step appends one token per sequence, so step i attends over
+``context_lens + i`` tokens; every step's metadata (slots, tables, lengths)
+is uploaded to HBM before timing starts.  As in a model with several layers,
+consecutive steps read different KV pools: ``--layers`` copies of the pool
+are made and step i uses copy ``i % layers``, so a step never finds the
+previous step's K/V in the 256 MiB Infinity Cache.  The timed region is
+exactly ``--steps`` back-to-back steps between two device synchronisations.
+
+Printed: one JSON line.  ``value`` is the achieved algorithmic HBM rate of
+the whole step (K/V rows of every attended token, once per KV head, plus the
+block-table entries read, plus the bytes the write / copy kernels move)
+divided by the step time.  ``roofline`` is the same figure for the decode
+kernel alone, from HIP events recorded on its stream around each launch.
+``cold_cache`` repeats the decode after reading a 1 GiB buffer before
+each call (evicts L2 and the Infinity Cache without leaving dirty lines).
+``cpu_baseline`` is the fp64 CPU oracle timed on this host on a bounded
+sample of the same step.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+                       [--partition P] [--no-cpu-baseline] [--cold-steps N]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and seqs·tokens/s attended"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+FLUSH_BYTES = 1 << 30      # > 4x the 256 MiB Infinity Cache
+CALIB_BYTES = 512 << 20    # plain copy of known size, read by the traffic counters
+
+# Decode launch configuration per workload (partition_size; 0 = one pass per
+# (sequence, KV head)).  The parity tests run the same configurations.
+WORKLOADS = {
+    "llama3_8b_b64": (lambda: W.c2_llama8b_b64(), 0),
+    "long_ctx_32k": (lambda: W.c3_long_context(), 512),
+    "mha_b256_bs8": (lambda: W.c5_mha_sweep(block_size=8), 0),
+    "mha_b256_bs16": (lambda: W.c5_mha_sweep(block_size=16), 0),
+    "mha_b256_bs32": (lambda: W.c5_mha_sweep(block_size=32), 0),
+    "tiny_f32": (lambda: W.c1_tiny_f32(), 0),
+}
+DEFAULT_WORKLOAD = "llama3_8b_b64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", "pa_decode.hip")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    p.add_argument("--partition", type=int, default=None,
+                   help="decode partition_size (default: the workload's configuration)")
+    p.add_argument("--cold-steps", type=int, default=10, help="cold-cache decode calls (0: skip)")
+    p.add_argument("--layers", type=int, default=4,
+                   help="KV pool copies that consecutive steps rotate over (1: same pool every step)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
+    return p.parse_args(argv)
+
+
+# --- step planning (host block manager) --------------------------------------------
+
+class StepPlan:
+    """Per-step metadata produced by the host block manager (row a1)."""
+
+    def __init__(self, case, nsteps, pkv):
+        bs = case.block_size
+        b = case.num_seqs
+        lens0 = case.context_lens.astype(np.int64)
+        # hand blocks out in the case's shuffled order: each sequence's own
+        # table first, then the rest of the pool
+        used = [int(x) for s in range(b) for x in case.block_tables[s, :W.ceil_div(lens0[s], bs)]]
+        rest = np.setdiff1d(np.arange(case.num_blocks), np.asarray(used, np.int64), assume_unique=False)
+        order = np.concatenate([np.asarray(used, np.int32), rest.astype(np.int32)])
+        need = int(sum(W.ceil_div(c + nsteps, bs) for c in lens0))
+        if need > case.num_blocks:
+            raise ValueError("pool too small for the planned steps")
+        pool = pkv.BlockPool(case.num_blocks, bs, order)
+        seqs = list(range(b))
+        for s in seqs:
+            pool.create(s, int(lens0[s]) - 1)
+        self.max_blocks = W.ceil_div(int(lens0.max()) + nsteps, bs)
+        self.slots, self.pairs, self.tables, self.lens = [], [], [], []
+        t0 = time.perf_counter()
+        for _ in range(nsteps):
+            slots, pairs = pool.append_batch(seqs)
+            tables, lens = pool.tables(seqs, self.max_blocks)
+            self.slots.append(slots.copy())
+            self.pairs.append(pairs.copy())
+            self.tables.append(tables)
+            self.lens.append(lens)
+        self.host_prep_us = (time.perf_counter() - t0) / max(nsteps, 1) * 1e6
+        pool.close()
+
+    def step_bytes(self, i, case):
+        """Algorithmic bytes of step i: (decode K/V + table, write, copy)."""
+        lens = self.lens[i].astype(np.int64)
+        elt = case.elt_bytes()
+        row = case.head_dim * elt
+        kv = int(lens.sum()) * case.num_kv_heads * 2 * row
+        table = 4 * int(sum(W.ceil_div(c, case.block_size) for c in lens))
+        ntok = int((self.slots[i] >= 0).sum())
+        write = ntok * case.num_kv_heads * row * 2 * 2 + 8 * len(self.slots[i])
+        block_bytes = case.num_kv_heads * case.block_size * row
+        copy = len(self.pairs[i]) * block_bytes * 2 * 2
+        return kv + table, write, copy
+
+
+# --- traffic counters (rocprofv3 --pmc summaries) -----------------------------------
+
+def source_digest():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, partition):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current decode source with this partition size."""
+    path = TRAFFIC_FILE.format(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*(\d+).*?source_sha256_16:\s*([0-9a-f]+).*?"
+                  r"partition_size:\s*(\d+)", text, re.S)
+    if not m or m.group(2) != source_digest() or int(m.group(3)) != partition:
+        return None
+    return int(m.group(1))
+
+
+# --- CPU baseline (oracle) -------------------------------------------------------------
+
+def cpu_baseline(case, plan, budget_s):
+    """fp64 oracle on the step-0 batch, sequence by sequence, until the time
+    budget is spent; rate scaled to the metric's unit."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as A
+
+    tables, lens = plan.tables[0], plan.lens[0]
+    elt = case.elt_bytes()
+    done_bytes, done_tok, n = 0, 0, 0
+    t0 = time.perf_counter()
+    while True:  # cycle over the batch until the budget is spent
+        s = n % case.num_seqs
+        A.decode(case.q[s:s + 1], case.k_cache, case.v_cache, tables[s:s + 1], lens[s:s + 1], case.scale,
+                 case.dtype)
+        c = int(lens[s])
+        done_bytes += c * case.num_kv_heads * 2 * case.head_dim * elt + 4 * W.ceil_div(c, case.block_size)
+        done_tok += c
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle, {n} sequence decodes cycling over the {case.num_seqs} sequences "
+                      f"of step 0 ({done_tok} tokens x {case.num_q_heads} q heads), {dt:.1f} s wall",
+            "tokens_per_s": round(done_tok / dt, 1), "seconds": round(dt, 2)}
+
+
+# --- main ------------------------------------------------------------------------------
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the decode path has no multi-GPU mode", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_354_amd as pkv
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    pkv.load()  # raises when the HIP library is missing: there is no other path
+    dev = torch.device("cuda:0")
+    make, default_part = WORKLOADS[args.workload]
+    partition = default_part if args.partition is None else args.partition
+
+    log(f"workload {args.workload}: drawing inputs")
+    case = make()
+    nplan = max(args.steps, args.warmup, 1)
+    plan = StepPlan(case, nplan, pkv)
+    log(f"planned {nplan} steps, host prep {plan.host_prep_us:.1f} us/step, pool {case.num_blocks} blocks")
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    k0, v0 = dev_t(case.k_cache), dev_t(case.v_cache)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.layers, 1) - 1)]
+    q, k_new, v_new = dev_t(case.q), dev_t(case.k_new), dev_t(case.v_new)
+    slots = [dev_t(x) for x in plan.slots]
+    tables = [dev_t(x) for x in plan.tables]
+    lens = [dev_t(x) for x in plan.lens]
+    pairs = [dev_t(x.reshape(-1, 2).astype(np.int64)) for x in plan.pairs]
+    max_ctx = [int(x.max()) for x in plan.lens]
+    out = torch.empty_like(q)
+    ws_bytes = pkv.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
+                                             max(max_ctx), partition)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if partition else None
+
+    steps = []
+    for i in range(nplan):
+        k_cache, v_cache = layers[i % len(layers)]
+        steps.append((pkv.prepare_copy_blocks(k_cache, v_cache, pairs[i]),
+                      pkv.prepare_write_kv(k_new, v_new, slots[i], k_cache, v_cache),
+                      pkv.prepare_decode(q, k_cache, v_cache, tables[i], lens[i], max_ctx[i], case.scale, out,
+                                         partition_size=partition, workspace=ws)))
+
+    # calibration copy of known size for the traffic counters (untimed)
+    calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    del calib_src, calib_dst
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        for call in steps[i % nplan]:
+            call()
+    torch.cuda.synchronize()
+
+    log(f"timed {args.steps} steps, partition_size {partition}")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        copy, write, decode = steps[i]
+        copy()
+        write()
+        ev[i][0].record()
+        decode()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+
+    totals = [plan.step_bytes(i, case) for i in range(args.steps)]
+    step_bytes = sum(sum(t) for t in totals)
+    dec_bytes = [t[0] for t in totals]
+    tokens = sum(int(plan.lens[i].astype(np.int64).sum()) for i in range(args.steps))
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / wall / 1e9
+    dec_avg_s = float(np.mean(dec_ms)) / 1e3
+    achieved = float(np.mean(dec_bytes)) / dec_avg_s / 1e9
+
+    cold = None
+    if args.cold_steps > 0:
+        n = args.cold_steps
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            flush_sum = flush.sum()  # reads 1 GiB: evicts L2 and the Infinity Cache (untimed)
+            cev[i][0].record()
+            steps[0][2]()
+            cev[i][1].record()
+        torch.cuda.synchronize()
+        cms = [a.elapsed_time(b) for a, b in cev]
+        cold = {"decode_us_median": round(float(np.median(cms)) * 1e3, 2),
+                "decode_us_p10": round(float(np.percentile(cms, 10)) * 1e3, 2),
+                "decode_us_p90": round(float(np.percentile(cms, 90)) * 1e3, 2),
+                "decode_GBps": round(dec_bytes[0] / (float(np.median(cms)) / 1e3) / 1e9, 1),
+                "frac_of_peak": round(dec_bytes[0] / (float(np.median(cms)) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del flush
+
+    traffic = measured_traffic(args.workload, partition)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block placement)",
+        "config": {
+            "workload": args.workload,
+            "num_seqs": case.num_seqs, "num_q_heads": case.num_q_heads,
+            "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+            "block_size": case.block_size, "pool_blocks": case.num_blocks,
+            "context_len_mean": round(float(plan.lens[0].mean()), 1),
+            "context_len_max": int(plan.lens[0].max()),
+            "partition_size": partition, "seed": case.meta.get("seed"),
+            "kv_pool_copies": len(layers),
+        },
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens / wall, 1),
+        "seq_steps_per_s": round(case.num_seqs * args.steps / wall, 1),
+        "step_bytes": int(step_bytes / args.steps),
+        "host_prep_us": round(plan.host_prep_us, 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel" + ("+merge_kernel" if partition else ""),
+            "avg_launch_us": round(dec_avg_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": int(np.mean(dec_bytes)),
+        },
+        "cold_cache": cold,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = cpu_baseline(case, plan, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

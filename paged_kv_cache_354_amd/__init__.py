@@ -405,3 +405,73 @@ class BlockPool:
 
     def tables(self, seqs, max_blocks, tables=None, context_lens=None):
         return pa_pool_tables(self.handle, seqs, max_blocks, tables, context_lens)
+
+
+# --- prepared calls ----------------------------------------------------------------
+#
+# A decode loop issues the same calls with the same buffers every step.  These
+# helpers check and marshal the arguments once and return a zero-argument
+# callable that only calls the C entry point (a few microseconds of host time),
+# so host overhead cannot hide the kernels' time.  The tensors must stay alive
+# and keep their shapes while the callable is used.
+
+def prepare_write_kv(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    t = int(slot_mapping.shape[0])
+    shape = (t, desc.num_kv_heads, desc.head_dim)
+    args = (_dev(k, "k", k_cache.dtype, shape), _dev(v, "v", k_cache.dtype, shape),
+            _dev(slot_mapping, "slot_mapping", torch.int64, (t,)), t, kp, vp, ctypes.byref(desc),
+            _stream(stream))
+    fn = load().pa_write_kv
+
+    def call():
+        _check(fn(*args))
+    call.keep = (desc, k, v, slot_mapping, k_cache, v_cache)
+    return call
+
+
+def prepare_copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    n = int(src_dst_pairs.shape[0])
+    if n == 0:
+        return lambda: None
+    args = (kp, vp, ctypes.byref(desc), _dev(src_dst_pairs, "src_dst_pairs", torch.int64, (n, 2)), n,
+            _stream(stream))
+    fn = load().pa_copy_blocks
+
+    def call():
+        _check(fn(*args))
+    call.keep = (desc, k_cache, v_cache, src_dst_pairs)
+    return call
+
+
+def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, out,
+                   partition_size=0, workspace=None, stream=None):
+    """``pa_decode`` with its arguments checked once; ``out`` and (when
+    partitioned) ``workspace`` must be given."""
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    b, hq, d = q.shape
+    if d != desc.head_dim:
+        raise ValueError("q head_dim does not match the pools")
+    mb = int(block_tables.shape[1]) if block_tables.dim() == 2 else -1
+    ws_need = pa_decode_workspace_bytes(b, hq, d, int(max_context_len), int(partition_size))
+    if workspace is not None:
+        wp, wbytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    else:
+        wp, wbytes = ctypes.c_void_p(0), 0
+    if wbytes < ws_need:
+        raise ValueError(f"workspace of {wbytes} bytes < {ws_need} needed")
+    args = (_dev(q, "q", k_cache.dtype), b, hq, kp, vp, ctypes.byref(desc),
+            _dev(block_tables, "block_tables", torch.int32, (b, mb)), mb,
+            _dev(context_lens, "context_lens", torch.int32, (b,)), int(max_context_len), float(scale),
+            int(partition_size), wp, wbytes, _dev(out, "out", out.dtype, (b, hq, d)), _dtype_code(out),
+            _stream(stream))
+    fn = load().pa_decode
+
+    def call():
+        _check(fn(*args))
+    call.keep = (desc, q, k_cache, v_cache, block_tables, context_lens, workspace, out)
+    return call
