@@ -26,7 +26,9 @@ Readings where the pages are silent (the same contract the C library states):
 * on copy-on-write the writing sequence receives the new private block and the
   other sharers keep the original (its count drops by one);
 * a block whose count is 1 is written in place, without a copy;
-* every failing call leaves the whole state unchanged.
+* every failing call leaves the whole state unchanged;
+* a batch append checks every sequence id before taking any block (an
+  unknown id is a state error even when the pool is also short).
 """
 
 import copy
@@ -131,7 +133,14 @@ class BlockManagerModel:
         return self._atomic(run)
 
     def append_batch(self, seqs):
-        """``append`` for each sequence in order; all-or-nothing."""
+        """``append`` for each sequence in order; all-or-nothing.
+
+        Every sequence id is checked before any block is taken, so a batch
+        naming an unknown sequence fails as a state error even when the pool
+        would also run short.
+        """
+        for s in seqs:
+            self._need(s)
         return self._atomic(lambda: [self.append(s) for s in seqs])
 
     def cow(self, seq, logical_block):
