@@ -24,7 +24,8 @@ Printed: one JSON line.  ``value`` is the achieved algorithmic HBM rate of
 the whole step (K/V rows of every attended token, once per KV head, plus the
 block-table entries read, plus the bytes the write / copy kernels move)
 divided by the step time.  ``roofline`` is the same figure for the decode
-kernel alone, from HIP events recorded on its stream around each launch.
+call alone (its kernels), from HIP events recorded on the launch stream
+around ``--steps`` back-to-back decode calls over the same per-step inputs.
 ``cold_cache`` repeats the decode after reading a 1 GiB buffer before
 each call (evicts L2 and the Infinity Cache without leaving dirty lines).
 ``cpu_baseline`` is the fp64 CPU oracle timed on this host on a bounded
@@ -55,19 +56,22 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, GB/s
 FLUSH_BYTES = 1 << 30      # > 4x the 256 MiB Infinity Cache
 CALIB_BYTES = 512 << 20    # plain copy of known size, read by the traffic counters
 
-# Decode launch configuration per workload (partition_size; 0 = one pass per
-# (sequence, KV head)).  The parity tests run the same configurations.
+# Decode launch configuration per workload (partition_size: -1 = the balanced
+# split, equal shares of all work per GPU workgroup slot).  The parity tests
+# run the same configurations.
+BALANCED = -1
 WORKLOADS = {
-    "llama3_8b_b64": (lambda: W.c2_llama8b_b64(), 0),
-    "long_ctx_32k": (lambda: W.c3_long_context(), 512),
-    "mha_b256_bs8": (lambda: W.c5_mha_sweep(block_size=8), 0),
-    "mha_b256_bs16": (lambda: W.c5_mha_sweep(block_size=16), 0),
-    "mha_b256_bs32": (lambda: W.c5_mha_sweep(block_size=32), 0),
-    "tiny_f32": (lambda: W.c1_tiny_f32(), 0),
+    "llama3_8b_b64": (lambda: W.c2_llama8b_b64(), BALANCED),
+    "long_ctx_32k": (lambda: W.c3_long_context(), BALANCED),
+    "mha_b256_bs8": (lambda: W.c5_mha_sweep(block_size=8), BALANCED),
+    "mha_b256_bs16": (lambda: W.c5_mha_sweep(block_size=16), BALANCED),
+    "mha_b256_bs32": (lambda: W.c5_mha_sweep(block_size=32), BALANCED),
+    "tiny_f32": (lambda: W.c1_tiny_f32(), BALANCED),
 }
 DEFAULT_WORKLOAD = "llama3_8b_b64"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
-DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", "pa_decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_decode_gqa.hip", "pa_decode_common.h")]
 
 
 def log(*a):
@@ -140,9 +144,23 @@ class StepPlan:
 
 # --- traffic counters (rocprofv3 --pmc summaries) -----------------------------------
 
+def decode_kernels(case, partition):
+    """Kernels one pa_decode call launches (the library's dispatch rule)."""
+    gqa = case.dtype == W.BF16 and case.num_q_heads // case.num_kv_heads in (4, 8) and case.head_dim in (64, 128, 256)
+    if gqa:
+        if partition == -1:
+            return "decode_gqa_balanced+merge_balanced_kernel"
+        return "decode_gqa_kernel" + ("+merge_kernel" if partition else "")
+    return "decode_kernel" + ("+merge_kernel" if partition > 0 else "")
+
+
 def source_digest():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the decode kernels' sources (the counters are tied to it)."""
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, partition):
@@ -153,7 +171,7 @@ def measured_traffic(workload, partition):
         return None
     text = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*(\d+).*?source_sha256_16:\s*([0-9a-f]+).*?"
-                  r"partition_size:\s*(\d+)", text, re.S)
+                  r"partition_size:\s*(-?\d+)", text, re.S)
     if not m or m.group(2) != source_digest() or int(m.group(3)) != partition:
         return None
     return int(m.group(1))
@@ -237,9 +255,9 @@ def main(argv=None):
     pairs = [dev_t(x.reshape(-1, 2).astype(np.int64)) for x in plan.pairs]
     max_ctx = [int(x.max()) for x in plan.lens]
     out = torch.empty_like(q)
-    ws_bytes = pkv.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim,
-                                             max(max_ctx), partition)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if partition else None
+    ws_bytes = pkv.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                             case.head_dim, max(max_ctx), partition)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     steps = []
     for i in range(nplan):
@@ -264,20 +282,25 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     log(f"timed {args.steps} steps, partition_size {partition}")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        copy, write, decode = steps[i]
-        copy()
-        write()
-        ev[i][0].record()
-        decode()
-        ev[i][1].record()
+        for call in steps[i]:
+            call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
+
+    # Decode launches alone, back to back, same per-step inputs: HIP events on
+    # the launch stream around the run give the average launch duration
+    # (an event between launches would add its own gap on the GPU).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        steps[i][2]()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_avg_s = e0.elapsed_time(e1) / 1e3 / args.steps
 
     totals = [plan.step_bytes(i, case) for i in range(args.steps)]
     step_bytes = sum(sum(t) for t in totals)
@@ -285,7 +308,6 @@ def main(argv=None):
     tokens = sum(int(plan.lens[i].astype(np.int64).sum()) for i in range(args.steps))
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / wall / 1e9
-    dec_avg_s = float(np.mean(dec_ms)) / 1e3
     achieved = float(np.mean(dec_bytes)) / dec_avg_s / 1e9
 
     cold = None
@@ -342,7 +364,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel" + ("+merge_kernel" if partition else ""),
+            "kernel": decode_kernels(case, partition),
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(np.mean(dec_bytes)),
         },

@@ -138,22 +138,35 @@ pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cache_t *cache
  *                 Lengths are clamped to min(max_context_len,
  *                 max_blocks_per_seq * block_size).
  *   scale         softmax scale (usually 1/sqrt(head_dim))
- *   partition_size 0: one pass per (sequence, KV head).  Otherwise a multiple
- *                 of block_size: each (sequence, KV head) context is split into
- *                 partitions of that many tokens, processed in parallel and
- *                 merged by a second kernel (online-softmax merge).
+ *   partition_size how each (sequence, KV head) context is cut into
+ *                 workgroup ranges:
+ *                 0: one range per (sequence, KV head), no workspace;
+ *                 a multiple of block_size: ranges of that many tokens,
+ *                   processed in parallel and merged by a second kernel
+ *                   (online-softmax merge);
+ *                 PA_PARTITION_BALANCED (-1): the library divides all
+ *                   (sequence, KV head, token) work into equal shares, one per
+ *                   workgroup slot of the GPU, and merges the sequences a
+ *                   share boundary cuts.  Used for bf16 pools with 4 or 8 query
+ *                   heads per KV head and up to 8192 sequences; other
+ *                   configurations run unpartitioned (or in 4096-token
+ *                   partitions when a context is too long for one workgroup).
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
- *                 bytes when partition_size > 0 (may be NULL otherwise); its
- *                 contents on entry do not matter.
+ *                 bytes, 256-byte aligned, when partition_size != 0 (may be
+ *                 NULL otherwise); its contents on entry do not matter.
  *   out           device [num_seqs][num_q_heads][head_dim] of out_dtype
  *                 (PA_F32, or the cache dtype).
  * num_q_heads must be a multiple of num_kv_heads, with a ratio of 1, 2, 4 or
  * 8.  Block ids outside [0, num_blocks) inside a sequence's length are a
  * precondition violation: the kernel stays inside the pools but that
- * sequence's output is unspecified.
+ * sequence's output is unspecified.  The result does not depend on where the
+ * blocks sit in the pool; it depends on partition_size only through fp32
+ * rounding of the summation order.
  * ------------------------------------------------------------------------ */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+#define PA_PARTITION_BALANCED (-1)
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
                       const void *k_cache, const void *v_cache, const pa_cache_t *cache,

@@ -30,6 +30,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_ENOMEM, PA_ESTATE, PA_EHIP = range(6)
 PA_F32, PA_BF16 = 0, 1
+PA_PARTITION_BALANCED = -1  # pa_decode: equal shares of all work per GPU workgroup slot
 
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "ENOMEM", 4: "ESTATE", 5: "EHIP"}
 
@@ -64,7 +65,7 @@ _SIGS = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_write_kv": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp, _i32,
                          ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
@@ -189,9 +190,10 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
                                  _stream(stream)))
 
 
-def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size):
-    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                                partition_size))
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                              partition_size):
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, partition_size))
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
@@ -200,9 +202,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
 
     ``q [B][Hq][d]`` in the cache dtype; ``block_tables int32 [B][MB]``;
     ``context_lens int32 [B]``; ``max_context_len`` a host int bounding every
-    length; ``partition_size`` 0 or a multiple of the block size (then a
-    uint8 ``workspace`` of ``pa_decode_workspace_bytes`` bytes is needed; one
-    is allocated here if not given).
+    length; ``partition_size`` 0, a multiple of the block size or
+    ``PA_PARTITION_BALANCED`` (the last two need a uint8 ``workspace`` of
+    ``pa_decode_workspace_bytes`` bytes; one is allocated here if not given).
     """
     torch = _torch()
     desc, kp, vp = _pools(k_cache, v_cache)
@@ -218,7 +220,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
     if out is None:
         out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
     op = _dev(out, "out", out_dtype, (b, hq, d))
-    ws_need = pa_decode_workspace_bytes(b, hq, d, int(max_context_len), int(partition_size))
+    ws_need = pa_decode_workspace_bytes(b, hq, desc.num_kv_heads, d, int(max_context_len),
+                                        int(partition_size))
     if partition_size and workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -457,7 +460,8 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_
     if d != desc.head_dim:
         raise ValueError("q head_dim does not match the pools")
     mb = int(block_tables.shape[1]) if block_tables.dim() == 2 else -1
-    ws_need = pa_decode_workspace_bytes(b, hq, d, int(max_context_len), int(partition_size))
+    ws_need = pa_decode_workspace_bytes(b, hq, desc.num_kv_heads, d, int(max_context_len),
+                                        int(partition_size))
     if workspace is not None:
         wp, wbytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     else:

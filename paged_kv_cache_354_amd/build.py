@@ -18,6 +18,7 @@ SOURCES = [
     "csrc/block_manager.cpp",
     "csrc/pa_cache_ops.hip",
     "csrc/pa_decode.hip",
+    "csrc/pa_decode_gqa.hip",
 ]
 ARCH = "gfx950"
 

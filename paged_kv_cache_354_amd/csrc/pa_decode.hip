@@ -29,48 +29,38 @@
 // Masking: tokens at or past the sequence length are never loaded and their
 // logits are -inf (selected, not multiplied), so whatever the tail slots of
 // the last block hold cannot reach the output.
+//
+// This vector-ALU kernel serves fp32 pools and bf16 pools with 1 or 2 query
+// heads per KV head; bf16 pools with 4 or 8 go to the matrix-core kernel in
+// pa_decode_gqa.hip.  Both write the same partition statistics, merged by
+// merge_kernel below.
 
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "pa.h"
+#include "pa_decode_common.h"
 #include "pa_status.h"
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+using pa::DecodeArgs;
+using pa::bf16_hi;
+using pa::bf16_lo;
+using pa::exp2_fast;
+using pa::group_sum;
+using pa::kLog2e;
+using pa::kMaxTableLds;
+using pa::kNegBig;
+using pa::kThreads;
+using pa::kWaves;
+using pa::store_out;
+using pa::xcd_work_id;
+
 constexpr int kLoadsPerTile = 4;             // 16-byte loads per lane per K (and V) tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;          // running-max start; finite keeps exp2 defined
-constexpr int kMaxTableLds = 4096;           // staged block ids per workgroup (16 KiB)
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-struct DecodeArgs {
-  const uint4 *q;
-  const uint4 *k_cache;
-  const uint4 *v_cache;
-  const int32_t *block_tables;
-  const int32_t *context_lens;
-  void *out;
-  float *part_m;   // [B][Hq][NP]
-  float *part_l;   // [B][Hq][NP]
-  float *part_o;   // [B][Hq][NP][D]
-  int32_t num_seqs;
-  int32_t num_q_heads;
-  int32_t num_kv_heads;
-  int32_t block_size;
-  int32_t log2_bs;
-  int32_t max_blocks;
-  int32_t num_blocks;
-  int32_t partition_size;  // tokens per partition (unpartitioned: >= every length)
-  int32_t num_parts;       // partitions per (sequence, KV head) in the grid
-  int32_t ctx_cap;         // lengths are clamped to this
-  int32_t out_f32;         // 1: fp32 output, 0: cache element type
-  float qscale;            // scale * log2(e)
-};
 
 template <typename E>
 struct Elt;
@@ -82,46 +72,6 @@ template <>
 struct Elt<uint16_t> {
   static constexpr int kVec = 8;
 };
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// fp32 -> bf16 pattern, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over aligned groups of LPR lanes; every lane of a group gets the same
-// value (each step adds a partner's value; a + b == b + a exactly).
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (LPR >= 2) x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]: partner lane ^ 1
-  if constexpr (LPR >= 4) x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]: partner lane ^ 2
-  if constexpr (LPR >= 8) x = dpp_add<0x141>(x);   // row_half_mirror: other quad of the 8
-  if constexpr (LPR >= 16) x = dpp_add<0x140>(x);  // row_mirror: other half of the 16
-  if constexpr (LPR >= 32) x += __shfl_xor(x, 16, 64);
-  if constexpr (LPR >= 64) x += __shfl_xor(x, 32, 64);
-  return x;
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup L runs on
-// XCD L % 8).  Renumber so that every XCD receives one contiguous range of
-// work ids: neighbouring work (same KV head, same partition) shares an L2.
-__device__ __forceinline__ int xcd_work_id(int L, int N) {
-  int xcd = L & 7, idx = L >> 3;
-  int q = N >> 3, r = N & 7;
-  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
 
 // Lane-owned query chunk for G heads, in the form the dot product wants.
 template <typename E, int G>
@@ -196,14 +146,6 @@ __device__ __forceinline__ void widen<uint16_t>(uint4 w, float (&f)[8]) {
   f[7] = bf16_hi(w.w);
 }
 
-template <typename E>
-__device__ __forceinline__ void store_out(void *out, size_t idx, float x, int out_f32) {
-  if (out_f32 || sizeof(E) == 4)
-    static_cast<float *>(out)[idx] = x;
-  else
-    static_cast<uint16_t *>(out)[idx] = to_bf16(x);
-}
-
 template <typename E, int D, int G, bool PART>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int VEC = Elt<E>::kVec;
@@ -274,8 +216,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       if (t < end) {
         const int blk = tbl[(t >> a.log2_bs) - first_blk];
         const size_t row = (size_t)blk * block_rows + head_rows + (t & (bs - 1));
-        kr[u] = kbase[row * LPR];
-        vr[u] = vbase[row * LPR];
+        kr[u] = pa::load_stream(kbase + row * LPR);
+        vr[u] = pa::load_stream(vbase + row * LPR);
       } else {
         kr[u] = make_uint4(0, 0, 0, 0);
         vr[u] = make_uint4(0, 0, 0, 0);
@@ -404,14 +346,10 @@ template <typename E, int D, int G>
 hipError_t launch(const DecodeArgs &a, bool part, int nblk_lds, hipStream_t st) {
   const int n_work = a.num_seqs * a.num_kv_heads * a.num_parts;
   const size_t lds = (size_t)nblk_lds * sizeof(int32_t);
-  if (part) {
+  if (part)
     hipLaunchKernelGGL((decode_kernel<E, D, G, true>), dim3(n_work), dim3(kThreads), lds, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<E, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, st, a);
-  } else {
+  else
     hipLaunchKernelGGL((decode_kernel<E, D, G, false>), dim3(n_work), dim3(kThreads), lds, st, a);
-  }
   return hipGetLastError();
 }
 
@@ -436,19 +374,48 @@ hipError_t launch_d(int d, int g, const DecodeArgs &a, bool part, int nblk_lds, 
   return hipErrorInvalidValue;
 }
 
+template <typename E>
+hipError_t launch_merge(int d, const DecodeArgs &a, hipStream_t st) {
+  const dim3 grid(a.num_seqs * a.num_q_heads);
+  switch (d) {
+    case 64: hipLaunchKernelGGL((merge_kernel<E, 64>), grid, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((merge_kernel<E, 128>), grid, dim3(128), 0, st, a); break;
+    case 256: hipLaunchKernelGGL((merge_kernel<E, 256>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WorkspaceLayout {
-  size_t m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, hdr_off, total;
 };
 
-WorkspaceLayout layout(int64_t b, int64_t hq, int64_t d, int64_t np) {
-  WorkspaceLayout w;
-  size_t ml = align256((size_t)(b * hq * np) * sizeof(float));
+// Partitioned: m, l [B][Hq][NP] and acc [B][Hq][NP][d], fp32.
+WorkspaceLayout partitioned_layout(int64_t b, int64_t hq, int64_t d, int64_t np) {
+  WorkspaceLayout w{};
+  const size_t ml = align256((size_t)(b * hq * np) * sizeof(float));
   w.m_off = 0;
   w.l_off = ml;
   w.o_off = 2 * ml;
   w.total = 2 * ml + align256((size_t)(b * hq * np * d) * sizeof(float));
+  return w;
+}
+
+// Balanced: header + [B + 1] prefix sums, then per slot (one per workgroup
+// plus one per (sequence, KV head)) m, l [G] and acc [G][d], fp32.
+WorkspaceLayout balanced_layout(int64_t b, int64_t hq, int64_t hkv, int64_t d) {
+  WorkspaceLayout w{};
+  const int64_t g = hq / hkv;
+  const int64_t slots = pa::kBalancedMaxWorkgroups + b * hkv;
+  w.hdr_off = 0;
+  const size_t hdr = align256((size_t)(pa::kBalancedHdrInts + b + 1) * sizeof(int32_t));
+  const size_t ml = align256((size_t)(slots * g) * sizeof(float));
+  w.m_off = hdr;
+  w.l_off = hdr + ml;
+  w.o_off = hdr + 2 * ml;
+  w.total = hdr + 2 * ml + align256((size_t)(slots * g * d) * sizeof(float));
   return w;
 }
 
@@ -457,13 +424,34 @@ int64_t parts_for(int64_t max_ctx, int64_t part) {
   return np < 1 ? 1 : np;
 }
 
+// Partition size the vector-ALU kernel uses when the balanced split is asked
+// for and its context does not fit one workgroup's table (a multiple of every
+// supported block size).
+constexpr int kValuBalancedFallbackP = 4096;
+
+bool uses_gqa_kernel(int dtype, int group, int head_dim) {
+  return dtype == PA_BF16 && pa::gqa_mfma_supported(group, head_dim);
+}
+
 }  // namespace
 
-extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                            int32_t max_context_len, int32_t partition_size) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  int64_t mc = max_context_len < 0 ? 0 : max_context_len;
-  return layout(num_seqs, num_q_heads, head_dim, parts_for(mc, partition_size)).total;
+extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t max_context_len,
+                                            int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads)
+    return 0;
+  const int64_t mc = max_context_len < 0 ? 0 : max_context_len;
+  if (partition_size > 0)
+    return partitioned_layout(num_seqs, num_q_heads, head_dim, parts_for(mc, partition_size)).total;
+  if (partition_size == PA_PARTITION_BALANCED) {
+    // whichever kernel runs: the balanced split, or the vector-ALU fallback
+    const size_t bal = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
+    const size_t fb =
+        partitioned_layout(num_seqs, num_q_heads, head_dim, parts_for(mc, kValuBalancedFallbackP)).total;
+    return bal > fb ? bal : fb;
+  }
+  return 0;
 }
 
 extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
@@ -492,18 +480,23 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
   const int g = num_q_heads / c.num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(PA_EUNSUPPORTED, "pa_decode: query heads per KV head = %d (built: 1, 2, 4, 8)", g);
-  if (partition_size < 0 || (partition_size % c.block_size))
-    return fail(PA_EINVAL, "pa_decode: partition_size %d must be 0 or a multiple of block_size %d",
+  if (partition_size != PA_PARTITION_BALANCED && (partition_size < 0 || (partition_size % c.block_size)))
+    return fail(PA_EINVAL,
+                "pa_decode: partition_size %d must be 0, PA_PARTITION_BALANCED or a multiple of "
+                "block_size %d",
                 partition_size, c.block_size);
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PA_EINVAL, "pa_decode: NULL pointer");
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
+    return fail(PA_EINVAL, "pa_decode: q and the pools must be 16-byte aligned");
 
   int log2_bs = 0;
   while ((1 << log2_bs) < c.block_size) ++log2_bs;
   const int64_t cap64 = (int64_t)max_blocks_per_seq * c.block_size;
   const int32_t ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
-  const bool part = partition_size > 0;
+  const int64_t ctx_blocks = ((int64_t)ctx_cap + c.block_size - 1) / c.block_size;
+  const bool gqa = uses_gqa_kernel(c.dtype, g, c.head_dim);
 
   DecodeArgs a{};
   a.q = (const uint4 *)q;
@@ -523,38 +516,79 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   a.qscale = scale * kLog2e;
 
-  int nblk_lds;
-  if (part) {
-    const int64_t np = parts_for(ctx_cap, partition_size);
-    const WorkspaceLayout wl = layout(num_seqs, num_q_heads, c.head_dim, np);
+  // How the contexts are cut into workgroup ranges.
+  int mode = pa::kModeUnpartitioned;
+  int32_t part = 0;
+  if (partition_size > 0) {
+    mode = pa::kModePartitioned;
+    part = partition_size;
+  } else if (partition_size == PA_PARTITION_BALANCED) {
+    if (gqa && num_seqs <= pa::kBalancedMaxSeqs) {
+      mode = pa::kModeBalanced;
+    } else if (!gqa && ctx_blocks > kMaxTableLds) {
+      mode = pa::kModePartitioned;
+      part = kValuBalancedFallbackP;
+    }
+  }
+  if (!gqa && mode == pa::kModePartitioned && part / c.block_size > kMaxTableLds)
+    return fail(PA_EUNSUPPORTED, "pa_decode: partition of %d blocks exceeds %d for this head configuration",
+                part / c.block_size, kMaxTableLds);
+  if (!gqa && mode == pa::kModeUnpartitioned && ctx_blocks > kMaxTableLds)
+    return fail(PA_EUNSUPPORTED,
+                "pa_decode: %lld blocks per sequence exceed %d for this head configuration; use a "
+                "partition_size",
+                (long long)ctx_blocks, kMaxTableLds);
+
+  const int64_t tbl_need = ctx_blocks < 1 ? 1 : ctx_blocks;
+  int nblk_lds = 0;  // vector-ALU kernel: table entries per workgroup
+  if (mode == pa::kModePartitioned) {
+    const int64_t np = parts_for(ctx_cap, part);
+    const WorkspaceLayout wl = partitioned_layout(num_seqs, num_q_heads, c.head_dim, np);
     if (!workspace || workspace_bytes < wl.total)
       return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes < %zu needed", workspace_bytes,
                   wl.total);
-    if ((uintptr_t)workspace % 16)
-      return fail(PA_EINVAL, "pa_decode: workspace must be 16-byte aligned");
-    a.partition_size = partition_size;
+    a.partition_size = part;
     a.num_parts = (int32_t)np;
     a.part_m = (float *)((char *)workspace + wl.m_off);
     a.part_l = (float *)((char *)workspace + wl.l_off);
     a.part_o = (float *)((char *)workspace + wl.o_off);
-    nblk_lds = partition_size / c.block_size;
+    nblk_lds = part / c.block_size;
+    const int64_t per_part = part / c.block_size;
+    a.tbl_cap = (int32_t)(per_part < kMaxTableLds ? per_part : kMaxTableLds);
+  } else if (mode == pa::kModeBalanced) {
+    const WorkspaceLayout wl = balanced_layout(num_seqs, num_q_heads, c.num_kv_heads, c.head_dim);
+    if (!workspace || workspace_bytes < wl.total)
+      return fail(PA_EINVAL, "pa_decode: workspace of %zu bytes < %zu needed", workspace_bytes,
+                  wl.total);
+    a.partition_size = ctx_cap > 0 ? ctx_cap : 1;
+    a.num_parts = 1;
+    a.bal_hdr = (int32_t *)((char *)workspace + wl.hdr_off);
+    a.part_m = (float *)((char *)workspace + wl.m_off);
+    a.part_l = (float *)((char *)workspace + wl.l_off);
+    a.part_o = (float *)((char *)workspace + wl.o_off);
+    a.tbl_cap = (int32_t)(tbl_need < kMaxTableLds ? tbl_need : kMaxTableLds);
   } else {
     a.partition_size = ctx_cap > 0 ? ctx_cap : 1;
     a.num_parts = 1;
-    nblk_lds = (ctx_cap + c.block_size - 1) / c.block_size;
+    nblk_lds = (int)ctx_blocks;
+    a.tbl_cap = (int32_t)(tbl_need < kMaxTableLds ? tbl_need : kMaxTableLds);
   }
-  if (nblk_lds > kMaxTableLds)
-    return fail(PA_EUNSUPPORTED,
-                "pa_decode: %d blocks per workgroup exceed %d; use a smaller partition_size",
-                nblk_lds, kMaxTableLds);
+  if (workspace && (uintptr_t)workspace % 256)
+    return fail(PA_EINVAL, "pa_decode: workspace must be 256-byte aligned");
   const int64_t n_work = (int64_t)num_seqs * c.num_kv_heads * a.num_parts;
-  if (n_work > 0x7fffffff) return fail(PA_EINVAL, "pa_decode: grid of %lld workgroups too large", (long long)n_work);
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
-    return fail(PA_EINVAL, "pa_decode: q and the pools must be 16-byte aligned");
+  if (n_work > 0x7fffffff)
+    return fail(PA_EINVAL, "pa_decode: grid of %lld workgroups too large", (long long)n_work);
 
-  hipError_t e = c.dtype == PA_F32
-                     ? launch_d<float>(c.head_dim, g, a, part, nblk_lds, (hipStream_t)stream)
-                     : launch_d<uint16_t>(c.head_dim, g, a, part, nblk_lds, (hipStream_t)stream);
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (gqa)
+    e = pa::launch_decode_gqa(c.head_dim, g, a, mode, st);
+  else if (c.dtype == PA_BF16)
+    e = launch_d<uint16_t>(c.head_dim, g, a, mode == pa::kModePartitioned, nblk_lds, st);
+  else
+    e = launch_d<float>(c.head_dim, g, a, mode == pa::kModePartitioned, nblk_lds, st);
+  if (e == hipSuccess && mode == pa::kModePartitioned)
+    e = c.dtype == PA_BF16 ? launch_merge<uint16_t>(c.head_dim, a, st) : launch_merge<float>(c.head_dim, a, st);
   if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }

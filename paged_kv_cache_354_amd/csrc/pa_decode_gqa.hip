@@ -1,0 +1,549 @@
+// Grouped-query paged decode attention on the gfx950 matrix cores (bf16 pools).
+//
+// foundry "PagedAttention" ops page, "How it works": attention reads K/V
+// through the per-sequence block table, gathering scattered physical blocks,
+// and the math is that of one contiguous run: per (sequence, query head)
+// out = softmax(scale * q K^T) V, accumulated here in fp32 with an online
+// softmax (Milakov & Gimelshein 2018) in the exp2 domain.
+//
+// When G = Hq / Hkv query heads share one KV head, the logits of a 16-token
+// tile form a dense [G x d] x [d x 16] product; v_mfma_f32_16x16x32_bf16
+// computes it with the G heads in the M dimension (rows G..15 are zero) and
+// the 16 tokens in N.  That takes the dot products and their cross-lane sums
+// off the vector ALUs, which then only run the softmax and the P.V update.
+//
+// A workgroup (4 wave64s) runs one token range of one (sequence, KV head):
+// wave w takes tiles w, w + 4, ... of the range, two per loop iteration (the
+// loads of both are issued first, so the second tile's loads are in flight
+// while the first is computed; no load is in flight across the loop's back
+// edge, which keeps the compiler's waits exact).  The range's slice of the
+// block-table row is staged in LDS (in sub-ranges of at most tbl_cap
+// blocks).  Two ways of cutting the work into ranges:
+//   - grid: one workgroup per (sequence, KV head, partition of P tokens);
+//   - balanced: a grid of one resident workgroup per slot of the GPU, each
+//     taking an equal share of all (KV head, sequence, token) work in that
+//     order (lengths rounded up to 16), so no tail of lone long workgroups
+//     is left.  A workgroup that holds a whole sequence writes its output
+//     directly; sequences cut between workgroups are combined by
+//     merge_balanced_kernel.
+//
+// Lane layouts (lane l, 64 per wave):
+//   QK operands   g = l / 16, n = l % 16.  For k-step i, lane l holds 8 bf16
+//                 channels [8(4i + g), 8(4i + g) + 8) of token n's K row (one
+//                 16-byte load) and of query head n's q row (zero for n >= G).
+//                 The same (lane, slot) -> channel map on both operands makes
+//                 every output a full dot product.
+//   QK output     lane l, register j: head 4g + j, token n.
+//   PV            a V row is d bf16 = LPR lanes x 16 bytes; lane (r, c) =
+//                 (l / LPR, l % LPR) holds channels [8c, 8c + 8) of row r of
+//                 each load, RPW = 64 / LPR rows per load.  The tile's p
+//                 values go through a small per-wave LDS array to these lanes.
+//
+// The running max of every head is uniform across the wave (a row-wide max
+// after each tile), so the accumulator rescale factors are read into scalar
+// registers and skipped when no max moved.  Tokens at or past the end of the
+// range read a valid token's row instead (never outside the sequence's
+// blocks) and their logits are -inf by select, so tail slots cannot reach the
+// output.  V rows are streamed with non-temporal loads; K rows are read with
+// ordinary loads (each K load covers half of a 128-byte line of 16 rows, and
+// the line's other half is read by the next load from L2).
+
+#include "pa_decode_common.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;        // tokens per MFMA tile
+constexpr int kTilesPerIter = 2;
+
+template <int D, int G>
+struct GqaTile {
+  static constexpr int KSTEPS = D / 32;
+  static constexpr int LPR = D / 8;
+  static constexpr int RPW = 64 / LPR;
+  static constexpr int NV = kTile / RPW;
+  uint4 k[KSTEPS];
+  uint4 v[NV];
+};
+
+template <int D, int G, int NW>
+struct GqaShared {
+  float4 p[NW][kTile][G / 4];
+  float red_m[NW][G];
+  float red_l[NW][G];
+  float red_acc[NW][G][D];
+};
+
+// Attention of query heads [kvh G, kvh G + G) of sequence s over the tokens
+// [start, end) (0 <= start <= end <= the sequence's length, start a multiple
+// of 16): leaves every wave's (max, sum, acc) in sh.red_* and returns after a
+// barrier.  tbl has room for tbl_cap >= 1 block ids.
+// BIG: block_size >= 16, so a tile (16 tokens starting at a multiple of 16)
+// lies inside one block and needs one table lookup.  NW: waves per
+// workgroup; wave w takes tiles w, w + NW, ... (TPI of them per step), so the
+// summation order depends only on token positions.
+template <int D, int G, bool BIG, int NW, int TPI = kTilesPerIter>
+__device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, NW> &sh, int32_t *tbl,
+                                          int tbl_cap, int s, int kvh, int start, int end) {
+  using Tile = GqaTile<D, G>;
+  constexpr int KSTEPS = Tile::KSTEPS;
+  constexpr int LPR = Tile::LPR;
+  constexpr int RPW = Tile::RPW;
+  constexpr int NV = Tile::NV;
+  constexpr int HR = G / 4;  // 16-lane rows of the QK output that hold real heads
+  static_assert(G % 4 == 0 && G <= 16, "heads per KV head must be 4, 8, 12 or 16");
+  static_assert(NV * RPW == kTile, "a tile must be a whole number of V loads");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int r = lane / LPR;
+  const int c = lane % LPR;
+  const int bs = a.block_size;
+  const int log2_bs = a.log2_bs;
+
+  // q operand: head n of this KV head's group, channel chunks 4i + g.
+  const int h0 = kvh * G;
+  uint4 qop[KSTEPS];
+  {
+    const uint4 *qrow = a.q + ((size_t)s * a.num_q_heads + h0 + (n < G ? n : 0)) * LPR + g;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qop[i] = n < G ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
+  }
+
+  float m[4], l[4];  // running max / partial sum of head 4g + j (this lane's tokens)
+  float acc[G][8];   // PV accumulators: head h, channels [8c, 8c + 8) of the row group
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = kNegBig;
+    l[j] = 0.0f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+
+  const size_t block_rows = (size_t)a.num_kv_heads * bs;  // rows per physical block
+  const size_t head_rows = (size_t)kvh * bs;
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
+  int first_blk = 0;
+  int sub_end = start;
+
+  // Row index (in K/V rows of D elements) of a token of the staged sub-range.
+  auto token_row = [&](int t) -> size_t {
+    const int blk = tbl[(t >> log2_bs) - first_blk];
+    return (size_t)blk * block_rows + head_rows + (t & (bs - 1));
+  };
+
+  auto load_tile = [&](Tile &T, int t0) {
+    const int last = min(kTile, sub_end - t0) - 1;  // >= 0: t0 < sub_end
+    if constexpr (BIG) {
+      // t0 is a multiple of 16 and so is bs: the tile lies inside one block.
+      const int blk = __builtin_amdgcn_readfirstlane(tbl[(t0 >> log2_bs) - first_blk]);
+      const size_t row0 = (size_t)blk * block_rows + head_rows + (t0 & (bs - 1));
+      const uint4 *kt = a.k_cache + row0 * LPR;
+      const uint4 *vt = a.v_cache + row0 * LPR;
+      const int kofs = min(n, last) * LPR + g;
+#pragma unroll
+      for (int i = 0; i < KSTEPS; ++i) T.k[i] = kt[kofs + 4 * i];
+#pragma unroll
+      for (int u = 0; u < NV; ++u) T.v[u] = load_stream(vt + min(u * RPW + r, last) * LPR + c);
+    } else {
+      const uint4 *kt = a.k_cache + token_row(t0 + min(n, last)) * LPR + g;
+#pragma unroll
+      for (int i = 0; i < KSTEPS; ++i) T.k[i] = kt[4 * i];
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        T.v[u] = load_stream(a.v_cache + token_row(t0 + min(u * RPW + r, last)) * LPR + c);
+    }
+  };
+
+  auto compute_tile = [&](const Tile &T, int t0) {
+    const int nvalid = min(kTile, sub_end - t0);
+    f32x4_t sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qop[i]),
+                                                   __builtin_bit_cast(bf16x8_t, T.k[i]), sc, 0, 0, 0);
+    const bool valid = n < nvalid;
+    float pj[4], alpha[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float z = valid ? sc[j] * a.qscale : -INFINITY;
+      const float mn = fmaxf(m[j], row16_max(z));
+      alpha[j] = exp2_fast(m[j] - mn);
+      m[j] = mn;
+      pj[j] = exp2_fast(z - mn);
+      l[j] = fmaf(l[j], alpha[j], pj[j]);
+    }
+    if (g < HR) sh.p[wave][n][g] = make_float4(pj[0], pj[1], pj[2], pj[3]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // Rescale the accumulators by each head's factor (uniform across the wave).
+    float sa[G];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sa[h] = readlane_f(alpha[h & 3], 16 * (h >> 2));
+      moved |= sa[h] != 1.0f;
+    }
+    if (moved) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= sa[h];
+    }
+
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float4 pp[HR];
+#pragma unroll
+      for (int q4 = 0; q4 < HR; ++q4) pp[q4] = sh.p[wave][u * RPW + r][q4];
+      const uint4 w4 = T.v[u];
+      const float vf[8] = {bf16_lo(w4.x), bf16_hi(w4.x), bf16_lo(w4.y), bf16_hi(w4.y),
+                           bf16_lo(w4.z), bf16_hi(w4.z), bf16_lo(w4.w), bf16_hi(w4.w)};
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float4 &q4 = pp[h >> 2];
+        const float ph = (h & 3) == 0 ? q4.x : (h & 3) == 1 ? q4.y : (h & 3) == 2 ? q4.z : q4.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+      }
+    }
+    // the next tile's p must not overwrite this tile's before it is read
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  constexpr int kThr = 64 * NW;
+  constexpr int kStride = NW * kTile;
+  for (int sub = start; sub < end; sub = sub_end) {
+    // at most tbl_cap whole blocks; later sub-ranges start on a block boundary
+    first_blk = sub >> log2_bs;
+    sub_end = (int)min((int64_t)end, ((int64_t)first_blk + tbl_cap) << log2_bs);
+    const int nblk = ((sub_end - 1) >> log2_bs) - first_blk + 1;
+    for (int i = tid; i < nblk; i += kThr) {
+      const int b = trow[first_blk + i];
+      tbl[i] = (unsigned)b < (unsigned)a.num_blocks ? b : 0;  // stay inside the pool
+    }
+    __syncthreads();
+    for (int t0 = sub + wave * kTile; t0 < sub_end; t0 += TPI * kStride) {
+      Tile T[TPI];
+#pragma unroll
+      for (int k = 0; k < TPI; ++k) {
+        const int tk = t0 + k * kStride;
+        load_tile(T[k], tk < sub_end ? tk : t0);  // always a valid tile; unused past the end
+      }
+#pragma unroll
+      for (int k = 0; k < TPI; ++k) {
+        const int tk = t0 + k * kStride;
+        if (k == 0 || tk < sub_end) compute_tile(T[k], tk);
+      }
+    }
+    __syncthreads();  // the table may be restaged next
+  }
+
+  // Wave totals: l over the 16 token lanes of each row, acc over the row groups.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) l[j] = group_sum<16>(l[j]);
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+  if (r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sh.red_acc[wave][h][c * 8 + e] = acc[h][e];
+  }
+  if (g < HR && n == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sh.red_m[wave][4 * g + j] = m[j];
+      sh.red_l[wave][4 * g + j] = l[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Combines the waves' statistics of the range and writes, for each of the
+// G query heads j: the normalised output (final: element (j, ch) at out
+// index out_row + j * D + ch), or the unnormalised partial (max at
+// pm[j * sm], sum at pl[j * sm], acc at po[j * so + ch]).
+template <int D, int G, int NW>
+__device__ __forceinline__ void gqa_finish(const DecodeArgs &a, const GqaShared<D, G, NW> &sh, size_t out_row,
+                                           bool final, float *pm, float *pl, float *po, int sm, int so) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * NW) {
+    const int j = idx / D;
+    const int ch = idx % D;
+    float M = sh.red_m[0][j];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) M = fmaxf(M, sh.red_m[wv][j]);
+    float L = 0.0f, A = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      const float f = exp2_fast(sh.red_m[wv][j] - M);
+      L = fmaf(sh.red_l[wv][j], f, L);
+      A = fmaf(sh.red_acc[wv][j][ch], f, A);
+    }
+    if (final) {
+      const float o = L > 0.0f ? A / L : 0.0f;
+      store_out<uint16_t>(a.out, out_row + (size_t)j * D + ch, o, a.out_f32);
+    } else {
+      po[(size_t)j * so + ch] = A;
+      if (ch == 0) {
+        pm[(size_t)j * sm] = M;
+        pl[(size_t)j * sm] = L;
+      }
+    }
+  }
+}
+
+// One workgroup per (sequence, KV head, partition).
+template <int D, int G, bool PART, bool BIG>
+__global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
+  extern __shared__ int32_t tbl[];
+  __shared__ GqaShared<D, G, kWaves> sh;
+
+  const int n_work = a.num_seqs * a.num_kv_heads * a.num_parts;
+  const int w = xcd_work_id(blockIdx.x, n_work);
+  const int s = w % a.num_seqs;
+  const int rest = w / a.num_seqs;
+  const int p = rest % a.num_parts;
+  const int kvh = rest / a.num_parts;
+
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  const int start = p * a.partition_size;
+  const int end = min(ctx, start + a.partition_size);
+  if (PART && start >= end) return;  // no tokens: the merge never reads this slot
+
+  gqa_range<D, G, BIG, kWaves>(a, sh, tbl, a.tbl_cap, s, kvh, start, end);
+  const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
+  const size_t slot = head0 * a.num_parts + p;
+  gqa_finish<D, G, kWaves>(a, sh, head0 * D, !PART, a.part_m + slot, a.part_l + slot, a.part_o + slot * D,
+                   a.num_parts, a.num_parts * D);
+}
+
+// Index of the sequence holding flattened token r: the largest s < B with
+// cum[s] <= r (cum is non-decreasing, cum[0] = 0 <= r < cum[B]).
+__device__ __forceinline__ int find_seq(const int32_t *cum, int B, int r) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Balanced split: workgroup w takes flattened tokens [w chunk, (w + 1) chunk)
+// of (KV head, sequence, token), every length rounded up to 16, with chunk
+// = total / (grid size) rounded up to 16.  The grid is one wave of resident
+// workgroups.  A workgroup that holds a whole sequence writes its output; the
+// others write a partial (max, sum, acc) at slot w + (kvh B + s), distinct for
+// every (workgroup, sequence) pair because workgroup ranges and sequences
+// both advance with the flattened position.  Workgroup 0 also leaves the
+// split (chunk, padded-length sum, prefix sums) in the workspace header for
+// merge_balanced_kernel.
+template <int D, int G, bool BIG>
+__global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
+  extern __shared__ int32_t dyn[];
+  __shared__ GqaShared<D, G, kWaves> sh;
+  __shared__ int32_t wave_tot[kWaves];
+  __shared__ int32_t carry;
+  const int B = a.num_seqs;
+  int32_t *cum = dyn;                       // [B + 1]
+  int32_t *tbl = dyn + ((B + 1 + 3) & ~3);  // [a.tbl_cap]
+  const int tid = threadIdx.x;
+
+  // Padded lengths and their prefix sums, kThreads sequences at a time.
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < B; base += kThreads) {
+    const int s = base + tid;
+    int ctx = s < B ? a.context_lens[s] : 0;
+    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+    int v = (ctx + 15) & ~15;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {  // inclusive scan within the wave
+      const int o = __shfl_up(v, off, 64);
+      if ((tid & 63) >= off) v += o;
+    }
+    if ((tid & 63) == 63) wave_tot[tid >> 6] = v;
+    __syncthreads();
+    int add = carry;
+    for (int wv = 0; wv < (tid >> 6); ++wv) add += wave_tot[wv];
+    if (s < B) cum[s + 1] = v + add;
+    __syncthreads();
+    if (tid == kThreads - 1) carry = v + add;
+    __syncthreads();
+  }
+  if (tid == 0) cum[0] = 0;
+  __syncthreads();
+
+  const int sigma = cum[B];
+  const int64_t total = (int64_t)a.num_kv_heads * sigma;
+  const int64_t chunk = ((total + a.num_wg - 1) / a.num_wg + 15) & ~(int64_t)15;
+  if (blockIdx.x == 0) {
+    if (tid == 0) {
+      a.bal_hdr[0] = (int32_t)chunk;
+      a.bal_hdr[1] = sigma;
+    }
+    for (int i = tid; i <= B; i += kThreads) a.bal_hdr[kBalancedHdrInts + i] = cum[i];
+  }
+  if (total == 0) return;
+
+  const int64_t f1 = min(total, (int64_t)(blockIdx.x + 1) * chunk);
+  for (int64_t f = (int64_t)blockIdx.x * chunk; f < f1;) {
+    const int kvh = (int)(f / sigma);
+    const int rr = (int)(f - (int64_t)kvh * sigma);
+    const int s = find_seq(cum, B, rr);
+    const int t = rr - cum[s];
+    const int lp = cum[s + 1] - cum[s];
+    const int seg = (int)min((int64_t)(lp - t), f1 - f);
+    int ctx = a.context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+    const int e = max(t, min(ctx, t + seg));
+    gqa_range<D, G, BIG, kWaves>(a, sh, tbl, a.tbl_cap, s, kvh, t, e);
+    const bool final = t == 0 && seg == lp;
+    const size_t slot = ((size_t)blockIdx.x + (size_t)kvh * B + s) * G;
+    const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
+    gqa_finish<D, G, kWaves>(a, sh, head0 * D, final, a.part_m + slot, a.part_l + slot, a.part_o + slot * D,
+                             1, D);
+    __syncthreads();  // sh is reused by the next segment
+    f += seg;
+  }
+}
+
+// Combines the pieces of each sequence that the balanced split cut between
+// workgroups; one workgroup per (sequence, KV head).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) {
+  const int B = a.num_seqs;
+  const int s = blockIdx.x % B;
+  const int kvh = blockIdx.x / B;
+  const int32_t *cum = a.bal_hdr + kBalancedHdrInts;
+  const int64_t chunk = a.bal_hdr[0];
+  const int sigma = a.bal_hdr[1];
+  const int lp = cum[s + 1] - cum[s];
+  const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
+  if (lp == 0) {  // empty sequence: zeros
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+      store_out<uint16_t>(a.out, head0 * D + idx, 0.0f, a.out_f32);
+    return;
+  }
+  const int64_t first = (int64_t)kvh * sigma + cum[s];
+  const int64_t w1 = first / chunk;
+  const int64_t w2 = (first + lp - 1) / chunk;
+  if (w1 == w2) return;  // one workgroup held the whole sequence and wrote it
+  const size_t pair = (size_t)kvh * B + s;
+  // All loads of up to 4 pieces are issued together, then folded into a
+  // running (max, sum, acc): the latency is one round trip per 4 pieces.
+  constexpr int kBatch = 4;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int j = idx / D;
+    const int ch = idx % D;
+    float M = kNegBig, L = 0.0f, A = 0.0f;
+    for (int64_t w0 = w1; w0 <= w2; w0 += kBatch) {
+      float pm[kBatch], pl_[kBatch], po[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t w = w0 + u <= w2 ? w0 + u : w2;  // repeats are masked below
+        const size_t slot = (w + pair) * G + j;
+        pm[u] = a.part_m[slot];
+        pl_[u] = a.part_l[slot];
+        po[u] = a.part_o[slot * D + ch];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (w0 + u > w2) break;
+        const float mn = fmaxf(M, pm[u]);
+        const float f0 = exp2_fast(M - mn), f1 = exp2_fast(pm[u] - mn);
+        L = L * f0 + pl_[u] * f1;
+        A = A * f0 + po[u] * f1;
+        M = mn;
+      }
+    }
+    const float o = L > 0.0f ? A / L : 0.0f;
+    store_out<uint16_t>(a.out, head0 * D + idx, o, a.out_f32);
+  }
+}
+
+// Workgroups of a kernel that fit on the current device at once (cached per
+// kernel instance and device).
+template <typename K>
+int resident_workgroups(K kernel, int threads, size_t dyn_lds) {
+  static int cache[64][2] = {};  // [device] -> {dyn_lds + 1, workgroups}
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev][0] == (int)dyn_lds + 1) return cache[dev][1];
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return kBalancedMaxWorkgroups;
+  int n = per_cu * cus;
+  n = n < 1 ? 1 : (n > kBalancedMaxWorkgroups ? kBalancedMaxWorkgroups : n);
+  cache[dev][0] = (int)dyn_lds + 1;
+  cache[dev][1] = n;
+  return n;
+}
+
+template <int D, int G, bool BIG>
+hipError_t launch_dgb(const DecodeArgs &a0, int mode, hipStream_t st) {
+  DecodeArgs a = a0;
+  if (mode == kModeBalanced) {
+    const size_t lds = (size_t)(((a.num_seqs + 1 + 3) & ~3) + a.tbl_cap) * sizeof(int32_t);
+    a.num_wg = resident_workgroups(decode_gqa_balanced<D, G, BIG>, kThreads, lds);
+    hipLaunchKernelGGL((decode_gqa_balanced<D, G, BIG>), dim3(a.num_wg), dim3(kThreads), lds, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((merge_balanced_kernel<D, G>), dim3(a.num_seqs * a.num_kv_heads), dim3(kThreads), 0,
+                       st, a);
+    return hipGetLastError();
+  }
+  const int n_work = a.num_seqs * a.num_kv_heads * a.num_parts;
+  const size_t lds = (size_t)a.tbl_cap * sizeof(int32_t);
+  if (mode == kModePartitioned)
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, true, BIG>), dim3(n_work), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_gqa_kernel<D, G, false, BIG>), dim3(n_work), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs &a, int mode, hipStream_t st) {
+  return a.block_size >= kTile ? launch_dgb<D, G, true>(a, mode, st) : launch_dgb<D, G, false>(a, mode, st);
+}
+
+template <int D>
+hipError_t launch_d(int group, const DecodeArgs &a, int mode, hipStream_t st) {
+  switch (group) {
+    case 4: return launch_dg<D, 4>(a, mode, st);
+    case 8: return launch_dg<D, 8>(a, mode, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode_gqa(int head_dim, int group, const DecodeArgs &a, int mode, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_d<64>(group, a, mode, st);
+    case 128: return launch_d<128>(group, a, mode, st);
+    case 256: return launch_d<256>(group, a, mode, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

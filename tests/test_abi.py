@@ -43,8 +43,15 @@ def test_version_and_error_strings():
 
 def test_workspace_bytes_host_only():
     # partitioned: [B][Hq][NP] max + sum, [B][Hq][NP][d] accumulators, 256-byte aligned
-    n = pkv.pa_decode_workspace_bytes(8, 32, 128, 32768, 512)
+    n = pkv.pa_decode_workspace_bytes(8, 32, 8, 128, 32768, 512)
     np_ = 64
     ml = -(-(8 * 32 * np_ * 4) // 256) * 256
     assert n == 2 * ml + -(-(8 * 32 * np_ * 128 * 4) // 256) * 256
-    assert pkv.pa_decode_workspace_bytes(8, 32, 128, 32768, 0) == 0
+    assert pkv.pa_decode_workspace_bytes(8, 32, 8, 128, 32768, 0) == 0
+    # balanced: header + prefix sums, then (2048 workgroups + B * Hkv) slots of G heads
+    b, hq, hkv, d = 64, 32, 8, 128
+    slots = 2048 + b * hkv
+    up = lambda x: -(-x // 256) * 256
+    want = up((64 + b + 1) * 4) + 2 * up(slots * 4 * 4) + up(slots * 4 * d * 4)
+    assert pkv.pa_decode_workspace_bytes(b, hq, hkv, d, 4096, pkv.PA_PARTITION_BALANCED) == want
+    assert pkv.pa_decode_workspace_bytes(b, hq, 5, d, 4096, 0) == 0  # 32 / 5 heads: invalid

@@ -19,6 +19,8 @@ from gpu_cases import (DevCase, announce, check_decode, oracle_after_write, out_
 
 pytestmark = pytest.mark.gpu
 
+BAL = -1  # PA_PARTITION_BALANCED: equal shares of all work per workgroup slot
+
 
 def run_and_check(pkv, case, partitions, f32_out_too=True):
     dc = DevCase(case)
@@ -39,41 +41,44 @@ def run_and_check(pkv, case, partitions, f32_out_too=True):
 @pytest.mark.parametrize("seed", [1, 101, 102, 103])
 def test_tiny_f32(gpu_lib, seed):
     case = W.c1_tiny_f32(seed=seed)
-    run_and_check(gpu_lib, case, [0, 16, 32, 48, 112])
+    run_and_check(gpu_lib, case, [0, 16, 32, 48, 112, BAL])
 
 
 @pytest.mark.parametrize("seed", [2, 101, 102])
 def test_small_bf16_gqa4(gpu_lib, seed):
     case = small_bf16_case(seed)
-    run_and_check(gpu_lib, case, [0, 16, 64, 512])
+    run_and_check(gpu_lib, case, [0, 16, 64, 512, BAL])
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d,bs", [
     (W.BF16, 8, 8, 128, 8), (W.BF16, 8, 4, 128, 32), (W.BF16, 16, 2, 128, 16),
     (W.BF16, 4, 4, 64, 16), (W.BF16, 8, 2, 256, 16), (W.BF16, 4, 4, 128, 1),
     (W.BF16, 8, 4, 128, 2), (W.BF16, 4, 1, 64, 4), (W.F32, 8, 2, 64, 8), (W.F32, 4, 4, 128, 16),
-    (W.F32, 2, 1, 256, 32), (W.BF16, 8, 1, 128, 64), (W.BF16, 2, 2, 128, 256)])
+    (W.F32, 2, 1, 256, 32), (W.BF16, 8, 1, 128, 64), (W.BF16, 2, 2, 128, 256),
+    # grouped-query matrix-core kernel: G 4 / 8, d 64 / 128 / 256, blocks under 16 tokens
+    (W.BF16, 16, 4, 128, 8), (W.BF16, 16, 2, 64, 16), (W.BF16, 8, 1, 256, 32), (W.BF16, 8, 1, 128, 2),
+    (W.BF16, 8, 2, 64, 1), (W.BF16, 32, 8, 128, 16)])
 def test_shape_grid(gpu_lib, dtype, hq, hkv, d, bs):
     rng = np.random.default_rng(hq * 7 + d + bs)
     lens = [1, bs, bs + 1, 2 * bs - 1] + list(rng.integers(1, 400, size=4))
     case = W.make_case(f"grid_{dtype}_{hq}_{hkv}_{d}_{bs}", seed=int(rng.integers(1 << 30)), dtype=dtype,
                        context_lens=lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs)
     parts = [0, bs * max(1, 64 // bs), 256 if bs <= 256 else bs]
-    run_and_check(gpu_lib, case, sorted(set(parts)))
+    run_and_check(gpu_lib, case, sorted(set(parts)) + [BAL])
 
 
 def test_poisoned_tails_unused_blocks_and_write_slot(gpu_lib):
     case = small_bf16_case(7, poison=True)
-    run_and_check(gpu_lib, case, [0, 16, 128])
+    run_and_check(gpu_lib, case, [0, 16, 128, BAL])
     f32case = W.c1_tiny_f32(seed=9, poison=True)
-    run_and_check(gpu_lib, f32case, [0, 16])
+    run_and_check(gpu_lib, f32case, [0, 16, BAL])
 
 
 def test_table_padding_is_never_read(gpu_lib):
     # -1 padding plus extra columns beyond every sequence's blocks
     case = small_bf16_case(8, max_blocks=80)
     assert (case.block_tables[:, -1] == -1).all()
-    run_and_check(gpu_lib, case, [0, 32])
+    run_and_check(gpu_lib, case, [0, 32, BAL])
 
 
 def test_zero_and_one_token_sequences(gpu_lib):
@@ -81,7 +86,7 @@ def test_zero_and_one_token_sequences(gpu_lib):
     case = W.make_case("ctx01", seed=3, dtype=W.BF16, context_lens=[0, 1, 5, 0, 1],
                        num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16)
     dc = DevCase(case)
-    for p in (0, 16):
+    for p in (0, 16, BAL):
         out = dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy()
         assert not out[0].any() and not out[3].any()
         from oracle.numerics import to_f64
@@ -92,20 +97,23 @@ def test_zero_and_one_token_sequences(gpu_lib):
                 assert np.array_equal(out[s, h].astype(np.float64), v[blk, h // 4, 0])
 
 
-@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
-def test_needle_coverage(gpu_lib, dtype):
+@pytest.mark.parametrize("dtype,hq,bs", [(W.F32, 4, 16), (W.BF16, 4, 16), (W.BF16, 8, 16),
+                                         (W.BF16, 16, 16), (W.BF16, 8, 8)])
+def test_needle_coverage(gpu_lib, dtype, hq, bs):
     """q = 0 gives p = 1/ctx exactly; one-hot V probes every block, the first and
     last token and the tail, so a missed / duplicated / foreign token shows up
-    as an error >= 1/ctx."""
-    announce("needle", dtype)
-    bs, d, hkv = 16, 128 if dtype == W.BF16 else 64, 2
+    as an error >= 1/ctx.  Query heads per KV head 2, 4 and 8 cover both
+    decode kernels."""
+    announce("needle", dtype, hq, bs)
+    d, hkv = 128 if dtype == W.BF16 else 64, 2
+    grp = hq // hkv
     lens = [1, 17, 100, 257, 1000, 2049]
-    case = W.make_case("needle", seed=5, dtype=dtype, context_lens=lens, num_q_heads=4,
+    case = W.make_case("needle", seed=5, dtype=dtype, context_lens=lens, num_q_heads=hq,
                        num_kv_heads=hkv, head_dim=d, block_size=bs, poison=True)
     one = np.uint16(0x3F80) if dtype == W.BF16 else np.float32(1)
     zero = np.uint16(0) if dtype == W.BF16 else np.float32(0)
     case.q[...] = zero
-    expect = np.zeros((len(lens), 4, d))
+    expect = np.zeros((len(lens), hq, d))
     vc = case.v_cache
     for s, n in enumerate(lens):
         nb = W.ceil_div(n, bs)
@@ -116,7 +124,7 @@ def test_needle_coverage(gpu_lib, dtype):
         for j, t in enumerate(probes):
             for g in range(hkv):
                 vc[case.block_tables[s, t // bs], g, t % bs, (j + g) % d] = one
-                expect[s, 2 * g:2 * g + 2, (j + g) % d] = 1.0 / n
+                expect[s, grp * g:grp * g + grp, (j + g) % d] = 1.0 / n
     # the write puts the new token (position n - 1) back: make it zero except its probe
     case.k_new[...] = zero
     case.v_new[...] = zero
@@ -125,7 +133,7 @@ def test_needle_coverage(gpu_lib, dtype):
         case.v_new[s] = vc[blk, :, off, :]
     dc = DevCase(case)
     dc.write(gpu_lib)
-    for p in (0, 16, 512):
+    for p in (0, 16, 512, BAL):
         got = dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
         np.testing.assert_allclose(got, expect, rtol=1e-5, atol=1e-7)
 
@@ -146,7 +154,7 @@ def test_placement_permutation_is_bitwise_invariant(gpu_lib):
     da, db = DevCase(a), DevCase(b)
     da.write(gpu_lib)
     db.write(gpu_lib)
-    for p in (0, 64):
+    for p in (0, 64, BAL):
         oa = da.decode(gpu_lib, partition_size=p, out_dtype=torch.float32)
         ob = db.decode(gpu_lib, partition_size=p, out_dtype=torch.float32)
         assert torch.equal(oa, ob)
@@ -157,9 +165,22 @@ def test_partition_sizes_agree(gpu_lib):
     case = small_bf16_case(41, hi=3000)
     dc = DevCase(case)
     outs = [dc.decode(gpu_lib, partition_size=p, out_dtype=torch.float32).cpu().numpy()
-            for p in (0, 16, 64, 256, 1024)]
+            for p in (0, 16, 64, 256, 1024, BAL)]
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) < 2e-6
+
+
+def test_balanced_many_sequences_and_empty_ones(gpu_lib):
+    """More sequences than one scan pass of the balanced split (256), with
+    zero-length ones mixed in, and lengths that make share boundaries cut
+    sequences at many places."""
+    rng = np.random.default_rng(61)
+    lens = rng.integers(0, 90, size=600)
+    lens[::37] = 0
+    lens[5] = 1500
+    case = W.make_case("many_seqs", seed=62, dtype=W.BF16, context_lens=lens, num_q_heads=16,
+                       num_kv_heads=4, head_dim=128, block_size=16, poison=True)
+    run_and_check(gpu_lib, case, [0, BAL])
 
 
 def test_argument_errors(gpu_lib):
@@ -179,9 +200,10 @@ def test_argument_errors(gpu_lib):
 # --- full-size workloads, checked on sampled rows ----------------------------------
 
 @pytest.mark.parametrize("name,partition", [("llama3_8b_b64", 0), ("llama3_8b_b64", 512),
-                                            ("long_ctx_32k", 512), ("mha_b256_bs8", 0),
+                                            ("llama3_8b_b64", BAL), ("long_ctx_32k", 512),
+                                            ("long_ctx_32k", BAL), ("mha_b256_bs8", 0),
                                             ("mha_b256_bs16", 0), ("mha_b256_bs32", 0),
-                                            ("mha_b256_bs16", 256)])
+                                            ("mha_b256_bs16", 256), ("mha_b256_bs16", BAL)])
 def test_full_size_sampled(gpu_lib, name, partition):
     announce("full", name, "P", partition)
     if name == "llama3_8b_b64":
