@@ -96,7 +96,9 @@ __device__ __forceinline__ void set_progress_priority(float progress) {
 // Attention of query heads [kvh G, kvh G + G) of sequence s over the tokens
 // [start, end) (0 <= start <= end <= the sequence's length, start a multiple
 // of 16): leaves every wave's (max, sum, acc) in sh.red_* and returns after a
-// barrier.  tbl has room for tbl_cap >= 1 block ids.
+// barrier.  tbl has room for tbl_cap >= 1 block ids, staged here; tbl_cap = 0
+// means the caller already staged the range's block ids in tbl (entry 0 for
+// the block holding token start) and made them visible with a barrier.
 // BIG: block_size >= 16, so a tile (16 tokens starting at a multiple of 16)
 // lies inside one block and needs one table lookup.  NW: waves per
 // workgroup; wave w takes tiles w, w + NW, ... (TPI of them per step), so the
@@ -246,15 +248,19 @@ __device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, N
   constexpr int kThr = 64 * NW;
   constexpr int kStride = NW * kTile;
   for (int sub = start; sub < end; sub = sub_end) {
-    // at most tbl_cap whole blocks; later sub-ranges start on a block boundary
     first_blk = sub >> log2_bs;
-    sub_end = (int)min((int64_t)end, ((int64_t)first_blk + tbl_cap) << log2_bs);
-    const int nblk = ((sub_end - 1) >> log2_bs) - first_blk + 1;
-    for (int i = tid; i < nblk; i += kThr) {
-      const int b = trow[first_blk + i];
-      tbl[i] = (unsigned)b < (unsigned)a.num_blocks ? b : 0;  // stay inside the pool
+    if (tbl_cap > 0) {
+      // at most tbl_cap whole blocks; later sub-ranges start on a block boundary
+      sub_end = (int)min((int64_t)end, ((int64_t)first_blk + tbl_cap) << log2_bs);
+      const int nblk = ((sub_end - 1) >> log2_bs) - first_blk + 1;
+      for (int i = tid; i < nblk; i += kThr) {
+        const int b = trow[first_blk + i];
+        tbl[i] = (unsigned)b < (unsigned)a.num_blocks ? b : 0;  // stay inside the pool
+      }
+      __syncthreads();
+    } else {
+      sub_end = end;
     }
-    __syncthreads();
     for (int t0 = sub + wave * kTile; t0 < sub_end; t0 += TPI * kStride) {
       if (share_done >= 0) set_progress_priority((float)(share_done + (t0 - start)) * share_inv);
       Tile T[TPI];
@@ -269,7 +275,7 @@ __device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, N
         if (k == 0 || tk < sub_end) compute_tile(T[k], tk);
       }
     }
-    __syncthreads();  // the table may be restaged next
+    if (tbl_cap > 0) __syncthreads();  // the table may be restaged next
   }
 
   // Wave totals: l over the 16 token lanes of each row, acc over the row groups.
@@ -356,6 +362,14 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
                    a.num_parts, a.num_parts * D);
 }
 
+// A piece of a balanced share: tokens [t, e) of sequence s for KV head kvh
+// (e clipped to the sequence's length), seg flattened positions including
+// the padding, lp the padded length, nblk the blocks holding [t, e).
+struct BalSegment {
+  int kvh, s, t, e, seg, lp, nblk;
+};
+constexpr int kMaxListedSegs = 16;
+
 // Index of the sequence holding flattened token r: the largest s < B with
 // cum[s] <= r (cum is non-decreasing, cum[0] = 0 <= r < cum[B]).
 __device__ __forceinline__ int find_seq(const int32_t *cum, int B, int r) {
@@ -384,11 +398,17 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   __shared__ int32_t wave_tot[kWaves];
   __shared__ int32_t carry;
   const int B = a.num_seqs;
-  int32_t *cum = dyn;                       // [B + 1]
-  int32_t *tbl = dyn + ((B + 1 + 3) & ~3);  // [a.tbl_cap]
+  int32_t *cum = dyn;                         // [B + 1] prefix sums of padded lengths
+  int32_t *tbl = dyn + ((B + 1 + 3) & ~3);    // [a.tbl_cap]
+  uint8_t *pad = (uint8_t *)(tbl + a.tbl_cap);  // [B] padded minus clamped length, 0..15
   const int tid = threadIdx.x;
+  // Until its tiles start, a workgroup is at 0% of its share: top priority,
+  // or the waves of workgroups already streaming on the CU starve this
+  // prologue (measured: 3-4x longer for workgroups with several segments).
+  __builtin_amdgcn_s_setprio(3);
 
-  // Padded lengths and their prefix sums, kThreads sequences at a time.
+  // Lengths and the prefix sums of the padded lengths, kThreads sequences at
+  // a time.
   if (tid == 0) carry = 0;
   __syncthreads();
   for (int base = 0; base < B; base += kThreads) {
@@ -396,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
     int ctx = s < B ? a.context_lens[s] : 0;
     ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
     int v = (ctx + 15) & ~15;
+    if (s < B) pad[s] = (uint8_t)(v - ctx);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {  // inclusive scan within the wave
       const int o = __shfl_up(v, off, 64);
@@ -428,17 +449,63 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   const int64_t f0 = (int64_t)blockIdx.x * chunk;
   const int64_t f1 = min(total, f0 + chunk);
   const float share_inv = f1 > f0 ? 1.0f / (float)(f1 - f0) : 0.0f;
-  for (int64_t f = f0; f < f1;) {
-    const int kvh = (int)(f / sigma);
-    const int rr = (int)(f - (int64_t)kvh * sigma);
-    const int s = find_seq(cum, B, rr);
-    const int t = rr - cum[s];
-    const int lp = cum[s + 1] - cum[s];
-    const int seg = (int)min((int64_t)(lp - t), f1 - f);
-    int ctx = a.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-    const int e = max(t, min(ctx, t + seg));
-    gqa_range<D, G, BIG, kWaves>(a, sh, tbl, a.tbl_cap, s, kvh, t, e, (int)(f - f0), share_inv);
+  const int log2_bs = a.log2_bs;
+
+  // The share [f0, f1) falls into segments, one per (KV head, sequence):
+  // tokens [t, e) of the sequence (e clipped to its length), seg flattened
+  // positions including the padding.
+  const bool small = total <= 0x7fffffff;  // 32-bit division suffices
+  auto segment_at = [&](int64_t f) {
+    BalSegment g;
+    g.kvh = small ? (int)f / sigma : (int)(f / sigma);
+    const int rr = (int)(f - (int64_t)g.kvh * sigma);
+    g.s = find_seq(cum, B, rr);
+    g.t = rr - cum[g.s];
+    g.lp = cum[g.s + 1] - cum[g.s];
+    g.seg = (int)min((int64_t)(g.lp - g.t), f1 - f);
+    g.e = max(g.t, min(g.lp - pad[g.s], g.t + g.seg));
+    g.nblk = g.e > g.t ? ((g.e - 1) >> log2_bs) - (g.t >> log2_bs) + 1 : 0;
+    return g;
+  };
+
+  // One walk over the share lists its segments (the first kMaxListedSegs)
+  // and counts the block ids they need.  When the share has no more
+  // segments than that and their block ids fit in tbl together, they are all
+  // staged now in one pass, so that no segment after the first waits for a
+  // table load; otherwise each segment is found again and stages its own.
+  __shared__ BalSegment segs[kMaxListedSegs];
+  int nseg = 0, need = 0;
+  for (int64_t f = f0; f < f1; ++nseg) {
+    const BalSegment g = segment_at(f);
+    if (tid == 0 && nseg < kMaxListedSegs) segs[nseg] = g;
+    need += g.nblk;
+    f += g.seg;
+  }
+  const bool listed = nseg <= kMaxListedSegs;
+  const bool staged = listed && need <= a.tbl_cap;
+  __syncthreads();
+  if (staged) {
+    int off = 0;
+    for (int i = 0; i < nseg; ++i) {
+      const BalSegment g = segs[i];
+      const int32_t *trow = a.block_tables + (size_t)g.s * a.max_blocks + (g.t >> log2_bs);
+      for (int j = tid; j < g.nblk; j += kThreads) {
+        const int b = trow[j];
+        tbl[off + j] = (unsigned)b < (unsigned)a.num_blocks ? b : 0;  // stay inside the pool
+      }
+      off += g.nblk;
+    }
+    __syncthreads();
+  }
+
+  int off = 0;
+  int64_t f = f0;
+  for (int i = 0; f < f1; ++i) {
+    const BalSegment g = listed ? segs[i] : segment_at(f);
+    const int s = g.s, kvh = g.kvh, t = g.t, e = g.e, seg = g.seg, lp = g.lp;
+    gqa_range<D, G, BIG, kWaves>(a, sh, staged ? tbl + off : tbl, staged ? 0 : a.tbl_cap, s, kvh, t, e,
+                                 (int)(f - f0), share_inv);
+    off += g.nblk;
     const bool final = t == 0 && seg == lp;
     const size_t slot = ((size_t)blockIdx.x + (size_t)kvh * B + s) * G;
     const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
@@ -503,31 +570,56 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) 
   }
 }
 
-// Workgroups of a kernel that fit on the current device at once (cached per
-// kernel instance and device).
-template <typename K>
-int resident_workgroups(K kernel, int threads, size_t dyn_lds) {
-  static int cache[64][2] = {};  // [device] -> {dyn_lds + 1, workgroups}
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev][0] == (int)dyn_lds + 1) return cache[dev][1];
-  int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dyn_lds) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return kBalancedMaxWorkgroups;
-  int n = per_cu * cus;
-  n = n < 1 ? 1 : (n > kBalancedMaxWorkgroups ? kBalancedMaxWorkgroups : n);
-  cache[dev][0] = (int)dyn_lds + 1;
-  cache[dev][1] = n;
-  return n;
-}
+// Launch limits of one balanced-kernel instance on the current device: the
+// workgroups that fit on it at once for a given dynamic LDS size, and the
+// dynamic LDS a workgroup may take.  Queried once per (instance, device, LDS
+// size) and kept.
+template <int D, int G, bool BIG>
+struct BalancedLimits {
+  static int resident(int dev, size_t dyn_lds) {
+    static int cache[64][2] = {};  // [device] -> {dyn_lds + 1, workgroups}
+    if (cache[dev][0] == (int)dyn_lds + 1) return cache[dev][1];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gqa_balanced<D, G, BIG>, kThreads,
+                                                     dyn_lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return kBalancedMaxWorkgroups;
+    int n = per_cu * cus;
+    n = n < 1 ? 1 : (n > kBalancedMaxWorkgroups ? kBalancedMaxWorkgroups : n);
+    cache[dev][0] = (int)dyn_lds + 1;
+    cache[dev][1] = n;
+    return n;
+  }
+  static size_t max_dyn_lds(int dev) {
+    static size_t cache[64] = {};
+    if (cache[dev]) return cache[dev];
+    int max_lds = 0;
+    hipFuncAttributes fa{};
+    if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(decode_gqa_balanced<D, G, BIG>)) !=
+            hipSuccess)
+      return 64 * 1024 - 36 * 1024;  // the 64 KiB floor minus the largest static share
+    cache[dev] = max_lds > (int)fa.sharedSizeBytes ? (size_t)max_lds - fa.sharedSizeBytes : 1;
+    return cache[dev];
+  }
+};
 
 template <int D, int G, bool BIG>
 hipError_t launch_dgb(const DecodeArgs &a0, int mode, hipStream_t st) {
   DecodeArgs a = a0;
   if (mode == kModeBalanced) {
-    const size_t lds = (size_t)(((a.num_seqs + 1 + 3) & ~3) + a.tbl_cap) * sizeof(int32_t);
-    a.num_wg = resident_workgroups(decode_gqa_balanced<D, G, BIG>, kThreads, lds);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    // dynamic LDS: prefix sums [B + 1] and block ids [tbl_cap] (int32), then
+    // one padding byte per sequence.  Fewer staged block ids when that would
+    // not fit, kept a multiple of 16 so that sub-ranges end on a tile.
+    const size_t fixed = (size_t)((a.num_seqs + 1 + 3) & ~3) * sizeof(int32_t) + ((a.num_seqs + 3) & ~3);
+    const size_t cap = BalancedLimits<D, G, BIG>::max_dyn_lds(dev);
+    if (fixed + kTile * sizeof(int32_t) > cap) return hipErrorInvalidConfiguration;
+    const size_t fit = ((cap - fixed) / sizeof(int32_t)) & ~(size_t)(kTile - 1);
+    if ((size_t)a.tbl_cap > fit) a.tbl_cap = (int32_t)fit;
+    const size_t lds = fixed + (size_t)a.tbl_cap * sizeof(int32_t);
+    a.num_wg = BalancedLimits<D, G, BIG>::resident(dev, lds);
     hipLaunchKernelGGL((decode_gqa_balanced<D, G, BIG>), dim3(a.num_wg), dim3(kThreads), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

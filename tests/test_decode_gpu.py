@@ -183,6 +183,43 @@ def test_balanced_many_sequences_and_empty_ones(gpu_lib):
     run_and_check(gpu_lib, case, [0, BAL])
 
 
+def test_balanced_workspace_reuse_garbage_and_repeats(gpu_lib):
+    """One balanced-split workspace, filled with random bytes first, serves
+    cases of different shapes in turn (one of them a single long sequence cut
+    into ~100 pieces per KV head), each with two query sets alternating, so
+    that a partial or split left by the previous call would show; every call
+    matches the unpartitioned kernel and repeats are bitwise equal."""
+    cases = [small_bf16_case(71), small_bf16_case(72, num_seqs=40, hi=300),
+             W.make_case("one_long", seed=73, dtype=W.BF16, context_lens=[30001], num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, block_size=16)]
+    dcs = [DevCase(c) for c in cases]
+    qsets = [(dc.q, torch.flip(dc.q, dims=[2]).contiguous()) for dc in dcs]
+    need = max(gpu_lib.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                                 c.max_context, BAL) for c in cases)
+    for fill in ("random", "zeros"):
+        if fill == "random":
+            ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+        else:
+            ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        first = {}
+        for rep in range(4):
+            for i, (c, dc) in enumerate(zip(cases, dcs)):
+                announce("workspace reuse", fill, rep, c.name)
+                q = qsets[i][rep % 2]
+                run = lambda p, ws_: gpu_lib.pa_decode(q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                                       dc.context_lens, c.max_context, c.scale,
+                                                       partition_size=p, workspace=ws_,
+                                                       out_dtype=torch.float32)
+                got = run(BAL, ws)
+                key = (i, rep % 2)
+                if key not in first:
+                    ref = run(0, None)
+                    assert torch.max(torch.abs(got - ref)).item() < 2e-6, (c.name, rep)
+                    first[key] = got
+                else:
+                    assert torch.equal(got, first[key]), (c.name, rep)
+
+
 def test_argument_errors(gpu_lib):
     announce("argument errors")
     case = small_bf16_case(51, num_seqs=2)
