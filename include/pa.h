@@ -148,9 +148,12 @@ pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cache_t *cache
  *                   (sequence, KV head, token) work into equal shares, one per
  *                   workgroup slot of the GPU, and merges the sequences a
  *                   share boundary cuts.  Used for bf16 pools with 4 or 8 query
- *                   heads per KV head and up to 8192 sequences; other
- *                   configurations run unpartitioned (or in 4096-token
- *                   partitions when a context is too long for one workgroup).
+ *                   heads per KV head, up to 8192 sequences and
+ *                   num_seqs * (max_context_len + 271) < 2^31; other
+ *                   configurations run unpartitioned, or in 4096-token
+ *                   partitions when a context is longer than that (vector-ALU
+ *                   kernel: longer than one workgroup's table).  The result
+ *                   is the same from call to call for the same inputs.
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes, 256-byte aligned, when partition_size != 0 (may be
  *                 NULL otherwise); its contents on entry do not matter.

@@ -424,9 +424,10 @@ int64_t parts_for(int64_t max_ctx, int64_t part) {
   return np < 1 ? 1 : np;
 }
 
-// Partition size the vector-ALU kernel uses when the balanced split is asked
-// for and its context does not fit one workgroup's table (a multiple of every
-// supported block size).
+// Partition size used when the balanced split is asked for but cannot run:
+// the vector-ALU kernel with a context beyond one workgroup's table, or a
+// batch whose prefix sums would not fit (a multiple of every supported block
+// size).
 constexpr int kValuBalancedFallbackP = 4096;
 
 bool uses_gqa_kernel(int dtype, int group, int head_dim) {
@@ -523,9 +524,13 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
     mode = pa::kModePartitioned;
     part = partition_size;
   } else if (partition_size == PA_PARTITION_BALANCED) {
-    if (gqa && num_seqs <= pa::kBalancedMaxSeqs) {
+    // the balanced split keeps the sequences' prefix sums (padded lengths
+    // plus a per-sequence cost of at most 256 positions) in int32 and in LDS
+    const bool fits = num_seqs <= pa::kBalancedMaxSeqs &&
+                      (int64_t)num_seqs * ((((int64_t)ctx_cap + 15) & ~(int64_t)15) + 256) <= 0x7fffffff;
+    if (gqa && fits) {
       mode = pa::kModeBalanced;
-    } else if (!gqa && ctx_blocks > kMaxTableLds) {
+    } else if (gqa ? ctx_cap > kValuBalancedFallbackP : ctx_blocks > kMaxTableLds) {
       mode = pa::kModePartitioned;
       part = kValuBalancedFallbackP;
     }

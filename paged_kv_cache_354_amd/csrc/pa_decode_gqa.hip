@@ -22,8 +22,8 @@
 //   - grid: one workgroup per (sequence, KV head, partition of P tokens);
 //   - balanced: a grid of one resident workgroup per slot of the GPU, each
 //     taking an equal share of all (KV head, sequence, token) work in that
-//     order (lengths rounded up to 16), so no tail of lone long workgroups
-//     is left.  A workgroup that holds a whole sequence writes its output
+//     order (lengths rounded up to 16, plus a fixed cost per sequence), so
+//     no tail of lone long workgroups is left.  A workgroup that holds a whole sequence writes its output
 //     directly; sequences cut between workgroups are combined by
 //     merge_balanced_kernel.
 //
@@ -362,6 +362,17 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
                    a.num_parts, a.num_parts * D);
 }
 
+// Every segment a workgroup takes on costs it a fixed time (its first loads
+// and the reduction at its end), so each nonempty sequence's flattened length
+// carries this many extra positions (no tokens) beyond its padding: shares
+// with more segments hold fewer tokens.  The cost is a fixed number of K/V
+// bytes, 48 KiB (96 tokens at head size 128: measured on MI355X on the
+// Llama-3-8B-shaped batch, 0 / 32 / 64 / 96 / 128 / 192 extra tokens gave
+// 109.8 / 109.0 / 108.3 / 107.5 / 108.2 / 108.5 us per call).
+template <int D>
+constexpr int kSegmentCost = ((48 * 1024 / (4 * D)) + 15) & ~15;
+static_assert(kSegmentCost<64> + 15 < 256, "padding must fit a byte");
+
 // A piece of a balanced share: tokens [t, e) of sequence s for KV head kvh
 // (e clipped to the sequence's length), seg flattened positions including
 // the padding, lp the padded length, nblk the blocks holding [t, e).
@@ -383,8 +394,8 @@ __device__ __forceinline__ int find_seq(const int32_t *cum, int B, int r) {
 }
 
 // Balanced split: workgroup w takes flattened tokens [w chunk, (w + 1) chunk)
-// of (KV head, sequence, token), every length rounded up to 16, with chunk
-// = total / (grid size) rounded up to 16.  The grid is one wave of resident
+// of (KV head, sequence, token), every nonempty length rounded up to 16 plus
+// kSegmentCost, with chunk = total / (grid size) rounded up to 16.  The grid is one wave of resident
 // workgroups.  A workgroup that holds a whole sequence writes its output; the
 // others write a partial (max, sum, acc) at slot w + (kvh B + s), distinct for
 // every (workgroup, sequence) pair because workgroup ranges and sequences
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   const int B = a.num_seqs;
   int32_t *cum = dyn;                         // [B + 1] prefix sums of padded lengths
   int32_t *tbl = dyn + ((B + 1 + 3) & ~3);    // [a.tbl_cap]
-  uint8_t *pad = (uint8_t *)(tbl + a.tbl_cap);  // [B] padded minus clamped length, 0..15
+  uint8_t *pad = (uint8_t *)(tbl + a.tbl_cap);  // [B] padded minus clamped length
   const int tid = threadIdx.x;
   // Until its tiles start, a workgroup is at 0% of its share: top priority,
   // or the waves of workgroups already streaming on the CU starve this
@@ -415,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
     const int s = base + tid;
     int ctx = s < B ? a.context_lens[s] : 0;
     ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-    int v = (ctx + 15) & ~15;
+    int v = ctx > 0 ? ((ctx + 15) & ~15) + kSegmentCost<D> : 0;
     if (s < B) pad[s] = (uint8_t)(v - ctx);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {  // inclusive scan within the wave
@@ -502,22 +513,25 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   int64_t f = f0;
   for (int i = 0; f < f1; ++i) {
     const BalSegment g = listed ? segs[i] : segment_at(f);
-    const int s = g.s, kvh = g.kvh, t = g.t, e = g.e, seg = g.seg, lp = g.lp;
+    const int s = g.s, kvh = g.kvh, t = g.t, e = g.e, seg = g.seg;
+    f += seg;
+    const int ctx = g.lp - pad[s];
+    if (t >= ctx) continue;  // padding and segment cost only: no piece
     gqa_range<D, G, BIG, kWaves>(a, sh, staged ? tbl + off : tbl, staged ? 0 : a.tbl_cap, s, kvh, t, e,
-                                 (int)(f - f0), share_inv);
+                                 (int)(f - seg - f0), share_inv);
     off += g.nblk;
-    const bool final = t == 0 && seg == lp;
+    const bool final = t == 0 && e == ctx;
     const size_t slot = ((size_t)blockIdx.x + (size_t)kvh * B + s) * G;
     const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
     gqa_finish<D, G, kWaves>(a, sh, head0 * D, final, a.part_m + slot, a.part_l + slot, a.part_o + slot * D,
                              1, D);
     __syncthreads();  // sh is reused by the next segment
-    f += seg;
   }
 }
 
 // Combines the pieces of each sequence that the balanced split cut between
-// workgroups; one workgroup per (sequence, KV head).
+// workgroups; one workgroup per (sequence, KV head).  The holders are the
+// workgroups whose shares meet the sequence's tokens (not its padding).
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) {
   const int B = a.num_seqs;
@@ -526,16 +540,17 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) 
   const int32_t *cum = a.bal_hdr + kBalancedHdrInts;
   const int64_t chunk = a.bal_hdr[0];
   const int sigma = a.bal_hdr[1];
-  const int lp = cum[s + 1] - cum[s];
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
   const size_t head0 = (size_t)s * a.num_q_heads + (size_t)kvh * G;
-  if (lp == 0) {  // empty sequence: zeros
+  if (ctx == 0) {  // empty sequence: zeros
     for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
       store_out<uint16_t>(a.out, head0 * D + idx, 0.0f, a.out_f32);
     return;
   }
   const int64_t first = (int64_t)kvh * sigma + cum[s];
   const int64_t w1 = first / chunk;
-  const int64_t w2 = (first + lp - 1) / chunk;
+  const int64_t w2 = (first + ctx - 1) / chunk;
   if (w1 == w2) return;  // one workgroup held the whole sequence and wrote it
   const size_t pair = (size_t)kvh * B + s;
   // All loads of up to 4 pieces are issued together, then folded into a
