@@ -12,6 +12,10 @@ One *step* is one decode step of a batch, as a serving loop runs it:
   a4  pa_decode       (K1, plus the partition-merge kernel K1b when
       partition_size > 0)
 
+a3 and a4 are one call, pa_decode_write (the new tokens are stored inside
+the balanced decode kernel, which reads them from the input rows), unless
+``--separate-write`` asks for the two calls.
+
 Each step appends one token per sequence, so step i attends over
 ``context_lens + i`` tokens; every step's metadata (slots, tables, lengths)
 is uploaded to HBM before timing starts.  As in a model with several layers,
@@ -90,6 +94,8 @@ def parse_args(argv=None):
     p.add_argument("--layers", type=int, default=4,
                    help="KV pool copies that consecutive steps rotate over (1: same pool every step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--separate-write", action="store_true",
+                   help="pa_write_kv then pa_decode instead of one pa_decode_write call")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
     return p.parse_args(argv)
 
@@ -144,14 +150,17 @@ class StepPlan:
 
 # --- traffic counters (rocprofv3 --pmc summaries) -----------------------------------
 
-def decode_kernels(case, partition):
-    """Kernels one pa_decode call launches (the library's dispatch rule)."""
+def decode_kernels(case, partition, fused=False):
+    """Kernels one timed decode call launches (the library's dispatch rule);
+    with the fused write, the balanced kernel stores the tokens itself and
+    the other paths launch write_kv_kernel first."""
     gqa = case.dtype == W.BF16 and case.num_q_heads // case.num_kv_heads in (4, 8) and case.head_dim in (64, 128, 256)
+    if gqa and partition == -1:
+        return "decode_gqa_balanced+merge_balanced_kernel"
+    pre = "write_kv_kernel+" if fused else ""
     if gqa:
-        if partition == -1:
-            return "decode_gqa_balanced+merge_balanced_kernel"
-        return "decode_gqa_kernel" + ("+merge_kernel" if partition else "")
-    return "decode_kernel" + ("+merge_kernel" if partition > 0 else "")
+        return pre + "decode_gqa_kernel" + ("+merge_kernel" if partition else "")
+    return pre + "decode_kernel" + ("+merge_kernel" if partition > 0 else "")
 
 
 def source_digest():
@@ -259,13 +268,22 @@ def main(argv=None):
                                              case.head_dim, max(max_ctx), partition)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
 
+    # per step: (copy, write, decode); with the fused call the write is part
+    # of the decode call
+    fused = not args.separate_write
     steps = []
     for i in range(nplan):
         k_cache, v_cache = layers[i % len(layers)]
-        steps.append((pkv.prepare_copy_blocks(k_cache, v_cache, pairs[i]),
-                      pkv.prepare_write_kv(k_new, v_new, slots[i], k_cache, v_cache),
-                      pkv.prepare_decode(q, k_cache, v_cache, tables[i], lens[i], max_ctx[i], case.scale, out,
-                                         partition_size=partition, workspace=ws)))
+        if fused:
+            write = lambda: None
+            decode = pkv.prepare_decode_write(k_new, v_new, slots[i], q, k_cache, v_cache, tables[i], lens[i],
+                                              max_ctx[i], case.scale, out, partition_size=partition,
+                                              workspace=ws)
+        else:
+            write = pkv.prepare_write_kv(k_new, v_new, slots[i], k_cache, v_cache)
+            decode = pkv.prepare_decode(q, k_cache, v_cache, tables[i], lens[i], max_ctx[i], case.scale, out,
+                                        partition_size=partition, workspace=ws)
+        steps.append((pkv.prepare_copy_blocks(k_cache, v_cache, pairs[i]), write, decode))
 
     # calibration copy of known size for the traffic counters (untimed)
     calib_src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -304,7 +322,7 @@ def main(argv=None):
 
     totals = [plan.step_bytes(i, case) for i in range(args.steps)]
     step_bytes = sum(sum(t) for t in totals)
-    dec_bytes = [t[0] for t in totals]
+    dec_bytes = [t[0] + (t[1] if fused else 0) for t in totals]  # what the timed decode call moves
     tokens = sum(int(plan.lens[i].astype(np.int64).sum()) for i in range(args.steps))
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / wall / 1e9
@@ -350,7 +368,7 @@ def main(argv=None):
             "context_len_mean": round(float(plan.lens[0].mean()), 1),
             "context_len_max": int(plan.lens[0].max()),
             "partition_size": partition, "seed": case.meta.get("seed"),
-            "kv_pool_copies": len(layers),
+            "kv_pool_copies": len(layers), "write_fused_into_decode": fused,
         },
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / wall, 1),
@@ -364,7 +382,7 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": decode_kernels(case, partition),
+            "kernel": decode_kernels(case, partition, fused),
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(np.mean(dec_bytes)),
         },

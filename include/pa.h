@@ -179,6 +179,34 @@ pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
                       void *out, int32_t out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_decode_write -- pa_write_kv(k, v, slot_mapping, num_tokens) followed by
+ * pa_decode(...), as one call.
+ * (foundry PagedAttention page, "How it works": a decode step stores the new
+ * token's key and value in the sequence's current block, and attention then
+ * reads the whole context, that token included, through the block table.)
+ *
+ * Arguments: those of pa_write_kv (k, v, slot_mapping, num_tokens), then
+ * those of pa_decode; k_cache and v_cache are written.  The pools after the
+ * call and out are those of the two calls in sequence (bitwise), given this
+ * precondition: on the balanced path with num_tokens == num_seqs, token i
+ * must be sequence i's newest position, slot_mapping[i] being the slot the
+ * block table gives for position context_lens[i] - 1 (or < 0 to store
+ * nothing, only for a sequence of length 0).  That path is one kernel: the
+ * tokens are stored while it runs and the attention reads position
+ * context_lens[i] - 1 from k and v themselves.  Otherwise the call runs
+ * pa_write_kv, then pa_decode.  Errors: those of the two calls; with
+ * num_seqs == 0 only the store is done.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_mapping,
+                            int32_t num_tokens, const void *q, int32_t num_seqs,
+                            int32_t num_q_heads, void *k_cache, void *v_cache,
+                            const pa_cache_t *cache, const int32_t *block_tables,
+                            int32_t max_blocks_per_seq, const int32_t *context_lens,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void *workspace, size_t workspace_bytes, void *out,
+                            int32_t out_dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Host block manager (host memory only, no device calls).
  * (foundry PagedAttention page, "Concept", "How it works", "At a glance";
  * aiacademy lesson "Paged Attention", analogy table.)

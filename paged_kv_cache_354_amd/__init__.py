@@ -10,6 +10,7 @@ The functions carry the C names declared in ``include/pa.h``:
 * ``pa_write_kv``     -- new tokens' K/V into their slots
 * ``pa_copy_blocks``  -- whole-block copies for copy-on-write
 * ``pa_decode``       -- paged single-query decode attention
+* ``pa_decode_write`` -- ``pa_write_kv`` then ``pa_decode`` in one call
 * ``pa_decode_workspace_bytes``
 * ``pa_pool_*`` / ``pa_seq_*`` -- host block manager (free pool, reference
   counts, block tables, copy-on-write decisions)
@@ -68,6 +69,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp, _i32,
                          ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
+    "pa_decode_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp,
+                               _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_num_free": (_i32, [_vp]),
@@ -196,16 +199,11 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max
                                                 max_context_len, partition_size))
 
 
-def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-              partition_size=0, workspace=None, out=None, out_dtype=None, stream=None):
-    """Paged decode attention; returns ``out [B][Hq][d]``.
-
-    ``q [B][Hq][d]`` in the cache dtype; ``block_tables int32 [B][MB]``;
-    ``context_lens int32 [B]``; ``max_context_len`` a host int bounding every
-    length; ``partition_size`` 0, a multiple of the block size or
-    ``PA_PARTITION_BALANCED`` (the last two need a uint8 ``workspace`` of
-    ``pa_decode_workspace_bytes`` bytes; one is allocated here if not given).
-    """
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 partition_size, workspace, out, out_dtype, stream, allocate):
+    """Marshalled ``pa_decode`` arguments (which follow the new-token ones in
+    ``pa_decode_write``), allocating ``out`` and the workspace when
+    ``allocate`` and they are not given."""
     torch = _torch()
     desc, kp, vp = _pools(k_cache, v_cache)
     b, hq, d = q.shape
@@ -218,20 +216,59 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
     if out_dtype is None:
         out_dtype = q.dtype if out is None else out.dtype
     if out is None:
+        if not allocate:
+            raise ValueError("out must be given")
         out = torch.empty((b, hq, d), dtype=out_dtype, device=q.device)
     op = _dev(out, "out", out_dtype, (b, hq, d))
     ws_need = pa_decode_workspace_bytes(b, hq, desc.num_kv_heads, d, int(max_context_len),
                                         int(partition_size))
-    if partition_size and workspace is None:
+    if partition_size and workspace is None and allocate:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=q.device)
     if workspace is not None:
         wp = _dev(workspace, "workspace")
         wbytes = workspace.numel() * workspace.element_size()
     else:
         wp, wbytes = ctypes.c_void_p(0), 0
-    _check(load().pa_decode(qp, b, hq, kp, vp, ctypes.byref(desc), tp, mb, lp, int(max_context_len),
-                            float(scale), int(partition_size), wp, wbytes, op, _dtype_code(out),
-                            _stream(stream)))
+    if wbytes < ws_need:
+        raise ValueError(f"workspace of {wbytes} bytes < {ws_need} needed")
+    args = (qp, b, hq, kp, vp, ctypes.byref(desc), tp, mb, lp, int(max_context_len), float(scale),
+            int(partition_size), wp, wbytes, op, _dtype_code(out), _stream(stream))
+    return args, out, (desc, q, k_cache, v_cache, block_tables, context_lens, workspace, out)
+
+
+def _new_token_args(k, v, slot_mapping, k_cache):
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    t = int(slot_mapping.shape[0])
+    shape = (t, desc.num_kv_heads, desc.head_dim)
+    return (_dev(k, "k", k_cache.dtype, shape), _dev(v, "v", k_cache.dtype, shape),
+            _dev(slot_mapping, "slot_mapping", torch.int64, (t,)), t)
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+              partition_size=0, workspace=None, out=None, out_dtype=None, stream=None):
+    """Paged decode attention; returns ``out [B][Hq][d]``.
+
+    ``q [B][Hq][d]`` in the cache dtype; ``block_tables int32 [B][MB]``;
+    ``context_lens int32 [B]``; ``max_context_len`` a host int bounding every
+    length; ``partition_size`` 0, a multiple of the block size or
+    ``PA_PARTITION_BALANCED`` (the last two need a uint8 ``workspace`` of
+    ``pa_decode_workspace_bytes`` bytes; one is allocated here if not given).
+    """
+    args, out, _ = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                partition_size, workspace, out, out_dtype, stream, True)
+    _check(load().pa_decode(*args))
+    return out
+
+
+def pa_decode_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                    scale, partition_size=0, workspace=None, out=None, out_dtype=None, stream=None):
+    """``pa_write_kv(k, v, slot_mapping)`` then ``pa_decode`` as one call (one
+    kernel on the balanced path when token i is sequence i's newest); the
+    arguments of the two, returns ``out``."""
+    args, out, _ = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                partition_size, workspace, out, out_dtype, stream, True)
+    _check(load().pa_decode_write(*_new_token_args(k, v, slot_mapping, k_cache), *args))
     return out
 
 
@@ -454,28 +491,25 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_
                    partition_size=0, workspace=None, stream=None):
     """``pa_decode`` with its arguments checked once; ``out`` and (when
     partitioned) ``workspace`` must be given."""
-    torch = _torch()
-    desc, kp, vp = _pools(k_cache, v_cache)
-    b, hq, d = q.shape
-    if d != desc.head_dim:
-        raise ValueError("q head_dim does not match the pools")
-    mb = int(block_tables.shape[1]) if block_tables.dim() == 2 else -1
-    ws_need = pa_decode_workspace_bytes(b, hq, desc.num_kv_heads, d, int(max_context_len),
-                                        int(partition_size))
-    if workspace is not None:
-        wp, wbytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
-    else:
-        wp, wbytes = ctypes.c_void_p(0), 0
-    if wbytes < ws_need:
-        raise ValueError(f"workspace of {wbytes} bytes < {ws_need} needed")
-    args = (_dev(q, "q", k_cache.dtype), b, hq, kp, vp, ctypes.byref(desc),
-            _dev(block_tables, "block_tables", torch.int32, (b, mb)), mb,
-            _dev(context_lens, "context_lens", torch.int32, (b,)), int(max_context_len), float(scale),
-            int(partition_size), wp, wbytes, _dev(out, "out", out.dtype, (b, hq, d)), _dtype_code(out),
-            _stream(stream))
+    args, _, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                 partition_size, workspace, out, None, stream, False)
     fn = load().pa_decode
 
     def call():
         _check(fn(*args))
-    call.keep = (desc, q, k_cache, v_cache, block_tables, context_lens, workspace, out)
+    call.keep = keep
+    return call
+
+
+def prepare_decode_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                         max_context_len, scale, out, partition_size=0, workspace=None, stream=None):
+    """``pa_decode_write`` with its arguments checked once."""
+    args, _, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                 partition_size, workspace, out, None, stream, False)
+    wargs = _new_token_args(k, v, slot_mapping, k_cache)
+    fn = load().pa_decode_write
+
+    def call():
+        _check(fn(*wargs, *args))
+    call.keep = keep + (k, v, slot_mapping)
     return call

@@ -455,12 +455,21 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   return 0;
 }
 
-extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
-                                 const void *k_cache, const void *v_cache, const pa_cache_t *cache,
-                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                 const int32_t *context_lens, int32_t max_context_len, float scale,
-                                 int32_t partition_size, void *workspace, size_t workspace_bytes,
-                                 void *out, int32_t out_dtype, void *stream) {
+namespace {
+
+// New tokens to store before attending (pa_decode_write), or none.
+struct NewTokens {
+  const void *k, *v;
+  const int64_t *slot_mapping;
+  int32_t num_tokens;
+  void *k_cache, *v_cache;
+};
+
+pa_status_t decode_call(const void *q, int32_t num_seqs, int32_t num_q_heads, const void *k_cache,
+                        const void *v_cache, const pa_cache_t *cache, const int32_t *block_tables,
+                        int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                        float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
+                        void *out, int32_t out_dtype, void *stream, const NewTokens *nt) {
   using pa::fail;
   if (!cache) return fail(PA_EINVAL, "pa_decode: cache descriptor is NULL");
   const pa_cache_t c = *cache;
@@ -486,7 +495,10 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
                 "pa_decode: partition_size %d must be 0, PA_PARTITION_BALANCED or a multiple of "
                 "block_size %d",
                 partition_size, c.block_size);
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0)  // nothing to attend; new tokens are still stored
+    return nt ? pa_write_kv(nt->k, nt->v, nt->slot_mapping, nt->num_tokens, nt->k_cache, nt->v_cache,
+                            cache, stream)
+              : PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return fail(PA_EINVAL, "pa_decode: NULL pointer");
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) % 16)
@@ -584,6 +596,22 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
   if (n_work > 0x7fffffff)
     return fail(PA_EINVAL, "pa_decode: grid of %lld workgroups too large", (long long)n_work);
 
+  // New tokens: stored by the balanced kernel itself when there is one per
+  // sequence, else by pa_write_kv before the attention.
+  if (nt) {
+    if (mode == pa::kModeBalanced && nt->num_tokens == num_seqs) {
+      if (((uintptr_t)nt->k | (uintptr_t)nt->v) % 16)
+        return fail(PA_EINVAL, "pa_decode_write: k and v must be 16-byte aligned");
+      a.k_new = (const uint4 *)nt->k;
+      a.v_new = (const uint4 *)nt->v;
+      a.slot_mapping = nt->slot_mapping;
+      a.num_slots = (int64_t)c.num_blocks * c.block_size;
+    } else if (pa_status_t ws = pa_write_kv(nt->k, nt->v, nt->slot_mapping, nt->num_tokens, nt->k_cache,
+                                            nt->v_cache, cache, stream)) {
+      return ws;
+    }
+  }
+
   const hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (gqa)
@@ -596,4 +624,34 @@ extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_
     e = c.dtype == PA_BF16 ? launch_merge<uint16_t>(c.head_dim, a, st) : launch_merge<float>(c.head_dim, a, st);
   if (e != hipSuccess) return fail(PA_EHIP, "pa_decode: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_decode(const void *q, int32_t num_seqs, int32_t num_q_heads,
+                                 const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *context_lens, int32_t max_context_len, float scale,
+                                 int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                 void *out, int32_t out_dtype, void *stream) {
+  return decode_call(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, scale, partition_size, workspace, workspace_bytes, out,
+                     out_dtype, stream, nullptr);
+}
+
+extern "C" pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_mapping,
+                                       int32_t num_tokens, const void *q, int32_t num_seqs,
+                                       int32_t num_q_heads, void *k_cache, void *v_cache,
+                                       const pa_cache_t *cache, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                       int32_t max_context_len, float scale, int32_t partition_size,
+                                       void *workspace, size_t workspace_bytes, void *out,
+                                       int32_t out_dtype, void *stream) {
+  if (num_tokens < 0) return pa::fail(PA_EINVAL, "pa_decode_write: num_tokens=%d < 0", num_tokens);
+  if (num_tokens > 0 && (!k || !v || !slot_mapping))
+    return pa::fail(PA_EINVAL, "pa_decode_write: NULL pointer");
+  const NewTokens nt{k, v, slot_mapping, num_tokens, k_cache, v_cache};
+  return decode_call(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables, max_blocks_per_seq,
+                     context_lens, max_context_len, scale, partition_size, workspace, workspace_bytes, out,
+                     out_dtype, stream, num_tokens > 0 ? &nt : nullptr);
 }

@@ -33,6 +33,10 @@ struct DecodeArgs {
   float *part_l;   // same shape as part_m
   float *part_o;   // partitioned: [B][Hq][NP][D]; balanced: [slots][G][D]
   int32_t *bal_hdr;  // balanced: {chunk, sum of padded lengths, ...}, then [B + 1] prefix sums
+  const uint4 *k_new;           // fused write: [B][Hkv][D] newest token of each sequence (or NULL)
+  const uint4 *v_new;           // fused write: same shape as k_new
+  const int64_t *slot_mapping;  // fused write: [B] pool slot of each sequence's newest token
+  int64_t num_slots;            // fused write: num_blocks * block_size
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;

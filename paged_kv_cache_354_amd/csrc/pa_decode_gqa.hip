@@ -106,10 +106,12 @@ __device__ __forceinline__ void set_progress_priority(float progress) {
 // share_done >= 0 turns on progress-driven wave priority: share_done is how
 // much of the workgroup's share (in tokens) came before this range and
 // share_inv the reciprocal of the share's size (see set_progress_priority).
+// newpos >= 0: the K and V rows of token newpos (in the range) are read from
+// a.k_new / a.v_new (row s, head kvh) instead of the pools.
 template <int D, int G, bool BIG, int NW, int TPI = kTilesPerIter>
 __device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, NW> &sh, int32_t *tbl,
                                           int tbl_cap, int s, int kvh, int start, int end,
-                                          int share_done = -1, float share_inv = 0.0f) {
+                                          int share_done = -1, float share_inv = 0.0f, int newpos = -1) {
   using Tile = GqaTile<D, G>;
   constexpr int KSTEPS = Tile::KSTEPS;
   constexpr int LPR = Tile::LPR;
@@ -182,6 +184,22 @@ __device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, N
 #pragma unroll
       for (int u = 0; u < NV; ++u)
         T.v[u] = load_stream(a.v_cache + token_row(t0 + min(u * RPW + r, last)) * LPR + c);
+    }
+  };
+
+  // The tile holding token newpos, whose K and V rows come from the input
+  // rows (row s, head kvh of a.k_new / a.v_new) instead of the pools.
+  auto load_tile_new = [&](Tile &T, int t0) {
+    const int last = min(kTile, sub_end - t0) - 1;
+    const size_t new_row = ((size_t)s * a.num_kv_heads + kvh) * LPR;
+    const int kt = t0 + min(n, last);
+    const uint4 *kp = kt == newpos ? a.k_new + new_row + g : a.k_cache + token_row(kt) * LPR + g;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) T.k[i] = kp[4 * i];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int vt = t0 + min(u * RPW + r, last);
+      T.v[u] = load_stream(vt == newpos ? a.v_new + new_row + c : a.v_cache + token_row(vt) * LPR + c);
     }
   };
 
@@ -261,19 +279,28 @@ __device__ __forceinline__ void gqa_range(const DecodeArgs &a, GqaShared<D, G, N
     } else {
       sub_end = end;
     }
-    for (int t0 = sub + wave * kTile; t0 < sub_end; t0 += TPI * kStride) {
+    // The tile holding newpos (the range's last: newpos = end - 1) is left
+    // out of the loop and done after it by the wave whose turn it is; it is
+    // that wave's last tile, so every wave's order is unchanged.
+    const int new_tile = newpos >= sub && newpos < sub_end ? newpos & ~(kTile - 1) : sub_end;
+    for (int t0 = sub + wave * kTile; t0 < new_tile; t0 += TPI * kStride) {
       if (share_done >= 0) set_progress_priority((float)(share_done + (t0 - start)) * share_inv);
       Tile T[TPI];
 #pragma unroll
       for (int k = 0; k < TPI; ++k) {
         const int tk = t0 + k * kStride;
-        load_tile(T[k], tk < sub_end ? tk : t0);  // always a valid tile; unused past the end
+        load_tile(T[k], tk < new_tile ? tk : t0);  // always a valid tile; unused past the end
       }
 #pragma unroll
       for (int k = 0; k < TPI; ++k) {
         const int tk = t0 + k * kStride;
-        if (k == 0 || tk < sub_end) compute_tile(T[k], tk);
+        if (k == 0 || tk < new_tile) compute_tile(T[k], tk);
       }
+    }
+    if (new_tile < sub_end && ((new_tile - sub) / kTile) % NW == wave) {
+      Tile T;
+      load_tile_new(T, new_tile);
+      compute_tile(T, new_tile);
     }
     if (tbl_cap > 0) __syncthreads();  // the table may be restaged next
   }
@@ -365,13 +392,16 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
 // Every segment a workgroup takes on costs it a fixed time (its first loads
 // and the reduction at its end), so each nonempty sequence's flattened length
 // carries this many extra positions (no tokens) beyond its padding: shares
-// with more segments hold fewer tokens.  The cost is a fixed number of K/V
-// bytes, 48 KiB (96 tokens at head size 128: measured on MI355X on the
-// Llama-3-8B-shaped batch, 0 / 32 / 64 / 96 / 128 / 192 extra tokens gave
-// 109.8 / 109.0 / 108.3 / 107.5 / 108.2 / 108.5 us per call).
+// with more segments hold fewer tokens.  The cost is 48 KiB of K/V, at most
+// 96 tokens (96 at head size 128: measured on MI355X on the Llama-3-8B-shaped
+// batch, 0 / 32 / 64 / 96 / 128 / 192 extra tokens gave 109.8 / 109.0 /
+// 108.3 / 107.5 / 108.2 / 108.5 us per call).
 template <int D>
-constexpr int kSegmentCost = ((48 * 1024 / (4 * D)) + 15) & ~15;
-static_assert(kSegmentCost<64> + 15 < 256, "padding must fit a byte");
+constexpr int kSegmentCost = 48 * 1024 / (4 * D) < 96 ? (48 * 1024 / (4 * D) + 15) & ~15 : 96;
+// The LDS byte per sequence holds padding + cost in bits 0..6 and, in bit 7,
+// whether its length was clamped (its newest token is then not attended).
+constexpr int kClampedBit = 0x80;
+static_assert(kSegmentCost<64> + 15 < kClampedBit, "padding must fit 7 bits");
 
 // A piece of a balanced share: tokens [t, e) of sequence s for KV head kvh
 // (e clipped to the sequence's length), seg flattened positions including
@@ -411,12 +441,39 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   const int B = a.num_seqs;
   int32_t *cum = dyn;                         // [B + 1] prefix sums of padded lengths
   int32_t *tbl = dyn + ((B + 1 + 3) & ~3);    // [a.tbl_cap]
-  uint8_t *pad = (uint8_t *)(tbl + a.tbl_cap);  // [B] padded minus clamped length
+  uint8_t *pad = (uint8_t *)(tbl + a.tbl_cap);  // [B] padded minus clamped length, kClampedBit
   const int tid = threadIdx.x;
   // Until its tiles start, a workgroup is at 0% of its share: top priority,
   // or the waves of workgroups already streaming on the CU starve this
   // prologue (measured: 3-4x longer for workgroups with several segments).
   __builtin_amdgcn_s_setprio(3);
+
+  // Fused write (a.k_new set): token s, the newest of sequence s, goes to
+  // pool slot slot_mapping[s] for every KV head (slots < 0 or outside the
+  // pool are skipped), tokens spread over the grid.  The attention below
+  // reads that token from k_new / v_new, never from the pools, so nothing in
+  // this kernel waits for these stores; their loads go out next to the
+  // first lengths' load.
+  const int ctx_first = tid < B ? a.context_lens[tid] : 0;
+  if (a.k_new) {
+    constexpr int kChunks = D / 8;  // 16-byte chunks per row
+    const int per_tok = a.num_kv_heads * kChunks;
+    for (int tok = blockIdx.x; tok < B; tok += gridDim.x) {
+      const int64_t slot = a.slot_mapping[tok];
+      for (int ch = tid; ch < per_tok; ch += kThreads) {
+        const uint4 kv = a.k_new[(size_t)tok * per_tok + ch];
+        const uint4 vv = a.v_new[(size_t)tok * per_tok + ch];
+        if (slot >= 0 && slot < a.num_slots) {
+          const int64_t blk = slot >> a.log2_bs;
+          const int64_t off = slot & (a.block_size - 1);
+          const size_t dst = ((size_t)(blk * a.num_kv_heads + ch / kChunks) * a.block_size + off) * kChunks +
+                             ch % kChunks;
+          const_cast<uint4 *>(a.k_cache)[dst] = kv;
+          const_cast<uint4 *>(a.v_cache)[dst] = vv;
+        }
+      }
+    }
+  }
 
   // Lengths and the prefix sums of the padded lengths, kThreads sequences at
   // a time.
@@ -424,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   __syncthreads();
   for (int base = 0; base < B; base += kThreads) {
     const int s = base + tid;
-    int ctx = s < B ? a.context_lens[s] : 0;
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+    const int raw = base == 0 ? ctx_first : (s < B ? a.context_lens[s] : 0);
+    const int ctx = raw < 0 ? 0 : (raw > a.ctx_cap ? a.ctx_cap : raw);
     int v = ctx > 0 ? ((ctx + 15) & ~15) + kSegmentCost<D> : 0;
-    if (s < B) pad[s] = (uint8_t)(v - ctx);
+    if (s < B) pad[s] = (uint8_t)((v - ctx) | (raw > a.ctx_cap ? kClampedBit : 0));
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {  // inclusive scan within the wave
       const int o = __shfl_up(v, off, 64);
@@ -474,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
     g.t = rr - cum[g.s];
     g.lp = cum[g.s + 1] - cum[g.s];
     g.seg = (int)min((int64_t)(g.lp - g.t), f1 - f);
-    g.e = max(g.t, min(g.lp - pad[g.s], g.t + g.seg));
+    g.e = max(g.t, min(g.lp - (pad[g.s] & (kClampedBit - 1)), g.t + g.seg));
     g.nblk = g.e > g.t ? ((g.e - 1) >> log2_bs) - (g.t >> log2_bs) + 1 : 0;
     return g;
   };
@@ -515,10 +572,13 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
     const BalSegment g = listed ? segs[i] : segment_at(f);
     const int s = g.s, kvh = g.kvh, t = g.t, e = g.e, seg = g.seg;
     f += seg;
-    const int ctx = g.lp - pad[s];
+    const int ctx = g.lp - (pad[s] & (kClampedBit - 1));
     if (t >= ctx) continue;  // padding and segment cost only: no piece
+    // with the fused write, the newest token (position ctx - 1 unless the
+    // length was clamped) comes from the input rows
+    const int newpos = a.k_new && e == ctx && !(pad[s] & kClampedBit) ? ctx - 1 : -1;
     gqa_range<D, G, BIG, kWaves>(a, sh, staged ? tbl + off : tbl, staged ? 0 : a.tbl_cap, s, kvh, t, e,
-                                 (int)(f - seg - f0), share_inv);
+                                 (int)(f - seg - f0), share_inv, newpos);
     off += g.nblk;
     const bool final = t == 0 && e == ctx;
     const size_t slot = ((size_t)blockIdx.x + (size_t)kvh * B + s) * G;
