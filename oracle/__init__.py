@@ -15,6 +15,10 @@ What it computes, and where the pages define it:
   through the table leaves the attention math unchanged.  The math itself is
   the textbook softmax(q K^T * scale) V, evaluated here in fp64 on a contiguous
   gather of each sequence's blocks.
+* ``prefill.prefill`` -- causal attention of a chunk of new queries per
+  sequence (a prompt, or its next piece) read through the block table: query
+  ``i`` of ``n`` sits at position ``ctx - n + i`` and sees keys ``0 .. that``
+  (foundry page, *Concept* and *How it works*; textbook causal softmax).
 * ``attention.partials`` / ``attention.merge`` -- the same result computed per
   context partition and merged (online-softmax normaliser merge,
   Milakov & Gimelshein 2018); exact in real arithmetic.
@@ -37,4 +41,4 @@ hand-worked golden fixtures under ``tests/golden/`` and invariants the pages
 state (placement independence, sharing, tail blocks).
 """
 
-from . import attention, block_manager, kvcache, numerics  # noqa: F401
+from . import attention, block_manager, kvcache, numerics, prefill  # noqa: F401
