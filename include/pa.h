@@ -207,6 +207,42 @@ pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_ma
                             int32_t out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_prefill -- causal attention of a chunk of new queries per sequence (a
+ * prompt, or its next piece), reading keys and values through the block table.
+ * (foundry PagedAttention page, Concept and How it works: a sequence's keys
+ * and values sit in the blocks its table names, wherever they are, and the
+ * attention reads them through the table; a prompt is many tokens at once.)
+ *
+ *   q             device [num_tokens][num_q_heads][head_dim], bf16; the
+ *                 queries of all sequences packed in sequence order.
+ *   cu_seqlens    device int32 [num_seqs + 1]: sequence s owns query rows
+ *                 cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (n_s of them),
+ *                 non-decreasing from 0; n_s <= max_query_len (a host bound;
+ *                 rows past it are not computed).
+ *   context_lens  device int32 [num_seqs]: keys of sequence s after its new
+ *                 tokens were stored (pa_write_kv); its n_s queries are its
+ *                 last n_s positions: query i sits at position
+ *                 context_lens[s] - n_s + i and attends to keys 0 .. that
+ *                 position (softmax(q K^T * scale) V).  A query at a
+ *                 position below 0 attends to nothing and its row is zero.
+ *   block_tables, max_blocks_per_seq, max_context_len: as for pa_decode
+ *                 (lengths are clamped to min(max_context_len,
+ *                 max_blocks_per_seq * block_size)).
+ *   out           device [num_tokens][num_q_heads][head_dim] of out_dtype
+ *                 (PA_F32 or PA_BF16).
+ * Built for bf16 pools, head_dim 64 or 128, 1, 2, 4 or 8 query heads per KV
+ * head and power-of-two block sizes up to 256; otherwise PA_EUNSUPPORTED.
+ * Scores and the softmax are fp32; the probabilities enter the product with
+ * V rounded to bf16.  num_seqs, num_tokens or max_query_len == 0: no-op.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num_q_heads,
+                       const int32_t *cu_seqlens, int32_t num_seqs, int32_t max_query_len,
+                       const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                       const int32_t *block_tables, int32_t max_blocks_per_seq,
+                       const int32_t *context_lens, int32_t max_context_len, float scale,
+                       void *out, int32_t out_dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Host block manager (host memory only, no device calls).
  * (foundry PagedAttention page, "Concept", "How it works", "At a glance";
  * aiacademy lesson "Paged Attention", analogy table.)

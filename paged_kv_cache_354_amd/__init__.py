@@ -11,6 +11,7 @@ The functions carry the C names declared in ``include/pa.h``:
 * ``pa_copy_blocks``  -- whole-block copies for copy-on-write
 * ``pa_decode``       -- paged single-query decode attention
 * ``pa_decode_write`` -- ``pa_write_kv`` then ``pa_decode`` in one call
+* ``pa_prefill``      -- causal paged attention of a chunk of new queries
 * ``pa_decode_workspace_bytes``
 * ``pa_pool_*`` / ``pa_seq_*`` -- host block manager (free pool, reference
   counts, block tables, copy-on-write decisions)
@@ -71,6 +72,8 @@ _SIGS = {
                          ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
     "pa_decode_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp,
                                _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
+    "pa_prefill": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp,
+                          _i32, ctypes.c_float, _vp, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_num_free": (_i32, [_vp]),
@@ -270,6 +273,51 @@ def pa_decode_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, conte
                                 partition_size, workspace, out, out_dtype, stream, True)
     _check(load().pa_decode_write(*_new_token_args(k, v, slot_mapping, k_cache), *args))
     return out
+
+
+def _prefill_args(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
+                  max_context_len, scale, out, out_dtype, stream):
+    torch = _torch()
+    desc, kp, vp = _pools(k_cache, v_cache)
+    t, hq, d = q.shape
+    if d != desc.head_dim:
+        raise ValueError("q head_dim does not match the pools")
+    b = int(context_lens.shape[0])
+    mb = int(block_tables.shape[1]) if block_tables.dim() == 2 else -1
+    if out_dtype is None:
+        out_dtype = q.dtype if out is None else out.dtype
+    if out is None:
+        out = torch.empty((t, hq, d), dtype=out_dtype, device=q.device)
+    args = (_dev(q, "q", k_cache.dtype), t, hq, _dev(cu_seqlens, "cu_seqlens", torch.int32, (b + 1,)), b,
+            int(max_query_len), kp, vp, ctypes.byref(desc),
+            _dev(block_tables, "block_tables", torch.int32, (b, mb)), mb,
+            _dev(context_lens, "context_lens", torch.int32, (b,)), int(max_context_len), float(scale),
+            _dev(out, "out", out_dtype, (t, hq, d)), _dtype_code(out), _stream(stream))
+    return args, out, (desc, q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, out)
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len, max_context_len,
+               scale, out=None, out_dtype=None, stream=None):
+    """Causal paged attention of packed queries ``q [T][Hq][d]`` (sequence s
+    owns rows ``cu_seqlens[s] .. cu_seqlens[s+1]-1``, its last positions);
+    returns ``out [T][Hq][d]``."""
+    args, out, _ = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
+                                 max_context_len, scale, out, out_dtype, stream)
+    _check(load().pa_prefill(*args))
+    return out
+
+
+def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
+                    max_context_len, scale, out, stream=None):
+    """``pa_prefill`` with its arguments checked once; ``out`` must be given."""
+    args, _, keep = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
+                                  max_context_len, scale, out, None, stream)
+    fn = load().pa_prefill
+
+    def call():
+        _check(fn(*args))
+    call.keep = keep
+    return call
 
 
 # --- host block manager ------------------------------------------------------------

@@ -19,6 +19,7 @@ SOURCES = [
     "csrc/pa_cache_ops.hip",
     "csrc/pa_decode.hip",
     "csrc/pa_decode_gqa.hip",
+    "csrc/pa_prefill.hip",
 ]
 ARCH = "gfx950"
 

@@ -1,0 +1,351 @@
+// pa_prefill: causal attention of a chunk of new queries per sequence (a
+// prompt, or its next piece) over the keys and values read through the
+// block table, on gfx950.
+//
+// (foundry PagedAttention page, Concept and How it works: every token's key
+// and value sit in the blocks the sequence's table names, and attention reads
+// them through the table; a prompt is many tokens at once.  The attention is
+// the textbook causal softmax: the query at position p sees keys 0..p.)
+//
+// One workgroup (4 wave64s) takes 16 query tokens of GW = min(G, 4) query
+// heads of one KV head (for G < 4, 4 / G blocks of 16 tokens), so that the
+// key/value tiles it stages in LDS serve 64 (token, head) rows.  Per tile of
+// 32 keys every wave computes, on the matrix cores (v_mfma_f32_16x16x32_bf16):
+//
+//   S^T = K Q^T       keys in M, the wave's 16 query rows in N, channels in K.
+//                     Lane (g, n) ends up with the scores of row n for keys
+//                     4g..4g+3 of each 16-key half.
+//   O^T += V^T P^T    channels in M (16 per block), rows in N, the 32 keys in
+//                     K.  The lane's 8 probabilities (keys 4g..4g+3 and
+//                     16+4g..16+4g+3, its own S^T entries rounded to bf16)
+//                     are exactly its B operand, so no value crosses lanes;
+//                     the A operand reads V^T from LDS in that key order.
+//
+// Every O^T value a lane holds belongs to its own row n, so the online
+// softmax rescale is lane-local; only the row max and the final row sum are
+// combined over the 4 lanes that share a row (lanes n, n+16, n+32, n+48).
+// The probabilities enter the PV product in bf16 (the usual flash-attention
+// trade: relative error up to 2^-9 per weight), the rest is fp32.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_decode_common.h"
+#include "pa_status.h"
+
+namespace {
+
+using pa::exp2_fast;
+using pa::kLog2e;
+using pa::kNegBig;
+using pa::load_stream;
+using pa::to_bf16;
+using pa::xcd_work_id;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;  // 4 wave64s
+constexpr int kKeys = 32;      // keys per tile
+constexpr int kVtRow = 40;     // bf16 per V^T row in LDS: 32 keys + 8 of padding (bank spread)
+
+struct PrefillArgs {
+  const uint4 *q;               // [T][Hq][D]
+  const uint4 *k_cache;         // [NB][Hkv][bs][D]
+  const uint4 *v_cache;
+  const int32_t *block_tables;  // [B][max_blocks]
+  const int32_t *context_lens;  // [B]
+  const int32_t *cu_seqlens;    // [B + 1]
+  void *out;                    // [T][Hq][D]
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t log2_bs;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t ctx_cap;   // lengths are clamped to this
+  int32_t q_blocks;  // query blocks per sequence in the grid
+  int32_t out_f32;   // 1: fp32 output, 0: bf16
+  float qscale;      // scale * log2(e)
+};
+
+template <int D>
+struct PrefillShared {
+  uint4 k[2][kKeys][D / 8 + 1];        // K rows of the tile (double buffer), 16 B of padding per row
+  uint16_t vt[2][D][kVtRow];           // V^T of the tile
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+  constexpr int GW = G < 4 ? G : 4;   // query heads per workgroup
+  constexpr int TQ = 16 * (4 / GW);   // query tokens per workgroup
+  constexpr int HG = G / GW;          // workgroups per (KV head, query block)
+  constexpr int C = D / 8;            // 16-byte chunks per row
+  constexpr int KSTEPS = D / 32;
+  constexpr int OB = D / 16;          // 16-channel blocks of the output
+  constexpr int NCH = kKeys * C / kThreads;  // staged chunks per thread and tile
+  static_assert(kKeys * C % kThreads == 0, "tile chunks must split evenly over the threads");
+  __shared__ PrefillShared<D> sh;
+
+  // Work order: head group, KV head, query block (last first: causal blocks
+  // near the end see the most keys), sequence; contiguous ranges per XCD so
+  // that the blocks sharing a (sequence, KV head) share an L2.
+  const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
+  int r = xcd_work_id(blockIdx.x, n_work);
+  const int hg = r % HG;
+  r /= HG;
+  const int kvh = r % a.num_kv_heads;
+  r /= a.num_kv_heads;
+  const int qb = a.q_blocks - 1 - r % a.q_blocks;
+  const int s = r / a.q_blocks;
+
+  const int lo = a.cu_seqlens[s];
+  const int n = a.cu_seqlens[s + 1] - lo;
+  const int q0 = qb * TQ;
+  if (q0 >= n) return;
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  const int first_pos = ctx - n;  // position of query 0 of the sequence
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int nl = lane & 15;
+  const int h = kvh * G + hg * GW + wave % GW;
+  const int tok0 = q0 + (wave / GW) * 16;  // the wave's first query
+  // keys the workgroup needs, and the ones this wave needs
+  const int kend = max(0, min(ctx, first_pos + min(q0 + TQ, n)));
+  const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16, n))) : 0;
+
+  // The lane's row (query tok, head h) and its last visible key.
+  const int tok = tok0 + nl;
+  const bool row_ok = tok < n;
+  const int prow = row_ok ? first_pos + tok : -1;
+
+  // B operand of S^T: channels [8(4i + g), +8) of the row's query.
+  uint4 qop[KSTEPS];
+  {
+    const uint4 *qrow = a.q + ((size_t)(lo + (row_ok ? tok : 0)) * a.num_q_heads + h) * C + g;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qop[i] = row_ok ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
+  }
+
+  f32x4_t o[OB];  // O^T: channel 16j + 4g + e of row nl
+#pragma unroll
+  for (int j = 0; j < OB; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = kNegBig, l = 0.0f;  // running max (shared by the row's 4 lanes) and this lane's sum
+
+  const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
+  const size_t block_rows = (size_t)a.num_kv_heads * a.block_size;
+  const size_t head_rows = (size_t)kvh * a.block_size;
+
+  // Staging: thread tid moves chunks tid, tid + 256, ... of the tile's
+  // kKeys x C chunks; keys at or past kend are zeros (never visible).
+  uint4 kreg[NCH], vreg[NCH];
+  auto load_tile = [&](int kt0) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int idx = tid + u * kThreads;
+      const int kk = kt0 + idx / C;
+      const int ch = idx % C;
+      if (kk < kend) {
+        int blk = trow[kk >> a.log2_bs];
+        blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;  // stay inside the pool
+        const size_t row = (size_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
+        kreg[u] = a.k_cache[row * C + ch];
+        vreg[u] = load_stream(a.v_cache + row * C + ch);
+      } else {
+        kreg[u] = make_uint4(0, 0, 0, 0);
+        vreg[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int idx = tid + u * kThreads;
+      const int key = idx / C;
+      const int ch = idx % C;
+      sh.k[b][key][ch] = kreg[u];
+      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sh.vt[b][8 * ch + 2 * e][key] = (uint16_t)(w[e] & 0xffffu);
+        sh.vt[b][8 * ch + 2 * e + 1][key] = (uint16_t)(w[e] >> 16);
+      }
+    }
+  };
+
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    const int kt0 = t * kKeys;
+    if (t + 1 < ntiles) load_tile(kt0 + kKeys);  // in flight during this tile's math
+    if (kt0 < wkend) {
+      // S^T for the two 16-key halves.
+      f32x4_t st[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        st[hh] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < KSTEPS; ++i)
+          st[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sh.k[b][16 * hh + nl][4 * i + g]),
+                                                           __builtin_bit_cast(bf16x8_t, qop[i]), st[hh], 0, 0, 0);
+      }
+      // Causal mask, running max over the row's 4 lanes, probabilities.
+      float z[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = kt0 + 16 * hh + 4 * g + e;
+          const float v = key <= prow ? st[hh][e] * a.qscale : -INFINITY;
+          z[4 * hh + e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2_fast(m - mn);
+      m = mn;
+      f32x8_t p;
+      float ps = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = exp2_fast(z[e] - mn);
+        ps += p[e];
+      }
+      l = fmaf(l, alpha, ps);
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int j = 0; j < OB; ++j) o[j] *= alpha;
+      }
+      const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);
+      // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
+#pragma unroll
+      for (int j = 0; j < OB; ++j) {
+        const uint16_t *vr = &sh.vt[b][16 * j + nl][0];
+        const uint2 k_lo = *reinterpret_cast<const uint2 *>(vr + 4 * g);
+        const uint2 k_hi = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * g);
+        const uint4 av = make_uint4(k_lo.x, k_lo.y, k_hi.x, k_hi.y);
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[j], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntiles) store_tile(b ^ 1);
+    __syncthreads();
+  }
+
+  // Row sums over the row's 4 lanes; normalised output.
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (row_ok) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const size_t base = ((size_t)(lo + tok) * a.num_q_heads + h) * D + 4 * g;
+#pragma unroll
+    for (int j = 0; j < OB; ++j) {
+      const f32x4_t v = o[j] * inv;
+      if (a.out_f32) {
+        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        const uint32_t w0 = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
+        const uint32_t w1 = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base + 16 * j) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_dg(const PrefillArgs &a, int n_work, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(n_work), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(int group, const PrefillArgs &a, int n_work, hipStream_t st) {
+  switch (group) {
+    case 1: return launch_dg<D, 1>(a, n_work, st);
+    case 2: return launch_dg<D, 2>(a, n_work, st);
+    case 4: return launch_dg<D, 4>(a, n_work, st);
+    case 8: return launch_dg<D, 8>(a, n_work, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num_q_heads,
+                                  const int32_t *cu_seqlens, int32_t num_seqs, int32_t max_query_len,
+                                  const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t max_context_len, float scale,
+                                  void *out, int32_t out_dtype, void *stream) {
+  using pa::fail;
+  if (!cache) return fail(PA_EINVAL, "pa_prefill: cache descriptor is NULL");
+  const pa_cache_t c = *cache;
+  if (num_tokens < 0 || num_seqs < 0 || max_query_len < 0 || max_context_len < 0 || num_q_heads <= 0 ||
+      c.num_blocks <= 0 || c.num_kv_heads <= 0 || c.block_size <= 0 || max_blocks_per_seq <= 0)
+    return fail(PA_EINVAL, "pa_prefill: sizes must be positive (counts may be 0)");
+  if (c.dtype != PA_BF16) return fail(PA_EUNSUPPORTED, "pa_prefill: cache dtype %d (built: bf16)", c.dtype);
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+    return fail(PA_EUNSUPPORTED, "pa_prefill: out dtype %d (use PA_F32 or PA_BF16)", out_dtype);
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(PA_EUNSUPPORTED, "pa_prefill: head_dim %d (built: 64, 128)", c.head_dim);
+  if (c.block_size > 256 || (c.block_size & (c.block_size - 1)))
+    return fail(PA_EUNSUPPORTED, "pa_prefill: block_size %d (powers of two up to 256)", c.block_size);
+  if (num_q_heads % c.num_kv_heads)
+    return fail(PA_EINVAL, "pa_prefill: %d query heads not a multiple of %d KV heads", num_q_heads,
+                c.num_kv_heads);
+  const int g = num_q_heads / c.num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_EUNSUPPORTED, "pa_prefill: query heads per KV head = %d (built: 1, 2, 4, 8)", g);
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!q || !cu_seqlens || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PA_EINVAL, "pa_prefill: NULL pointer");
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
+    return fail(PA_EINVAL, "pa_prefill: q, out and the pools must be 16-byte aligned");
+
+  int log2_bs = 0;
+  while ((1 << log2_bs) < c.block_size) ++log2_bs;
+  const int64_t cap64 = (int64_t)max_blocks_per_seq * c.block_size;
+  const int gw = g < 4 ? g : 4;
+  const int tq = 16 * (4 / gw);
+  PrefillArgs a{};
+  a.q = (const uint4 *)q;
+  a.k_cache = (const uint4 *)k_cache;
+  a.v_cache = (const uint4 *)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c.num_kv_heads;
+  a.block_size = c.block_size;
+  a.log2_bs = log2_bs;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = c.num_blocks;
+  a.ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
+  a.q_blocks = (max_query_len + tq - 1) / tq;
+  a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
+  a.qscale = scale * kLog2e;
+  const int64_t n_work = (int64_t)num_seqs * a.q_blocks * c.num_kv_heads * (g / gw);
+  if (n_work > 0x7fffffff)
+    return fail(PA_EINVAL, "pa_prefill: grid of %lld workgroups too large", (long long)n_work);
+
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t e = c.head_dim == 64 ? launch_d<64>(g, a, (int)n_work, st) : launch_d<128>(g, a, (int)n_work, st);
+  if (e != hipSuccess) return fail(PA_EHIP, "pa_prefill: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}

@@ -19,7 +19,7 @@ def declared():
 
 def test_header_declares_the_hot_path_calls():
     names = declared()
-    for n in ("pa_write_kv", "pa_decode", "pa_decode_write", "pa_copy_blocks", "pa_decode_workspace_bytes",
+    for n in ("pa_write_kv", "pa_decode", "pa_decode_write", "pa_prefill", "pa_copy_blocks", "pa_decode_workspace_bytes",
               "pa_pool_create", "pa_seq_append", "pa_seq_cow", "pa_seq_free"):
         assert n in names
 

@@ -1,0 +1,117 @@
+"""pa_prefill on the GPU against the fp64 prefill oracle.
+
+Tolerance, derived from the arithmetic (scores, softmax and sums in fp32;
+the probabilities enter the product with V rounded to bf16, relative error
+at most 2^-9 each, while the normaliser keeps them in fp32): the output is a
+weighted mean of value rows with weights off by at most 2^-9 relative, so
+
+    |gpu - ref| <= 2^-9 * max|V| + 1e-4          (fp32 output)
+    |gpu - ref| <= 2^-9 * max|V| + 2^-8 |ref| + 1e-4   (bf16 output)
+
+with max|V| over the values the sequence attends to, and 1e-4 for fp32
+accumulation order and exp2 (the decode kernels' fp32 bar).
+
+Cases cover whole prompts, chunks after a cached context, one query per
+sequence, empty chunks and chunks longer than the context (zero rows), on
+pools poisoned with NaN wherever no visible key lives.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import prefill as P
+
+from gpu_cases import DevCase, announce, oracle_after_write, out_to_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def make_prefill(seed, lens, nq, hq, hkv, d, bs, poison=True):
+    case = W.make_case(f"prefill_s{seed}", seed=seed, dtype=W.BF16, context_lens=lens, num_q_heads=hq,
+                       num_kv_heads=hkv, head_dim=d, block_size=bs, poison=poison)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    rng = np.random.default_rng(seed + 17)
+    q = W.normal(rng, (int(cu[-1]), hq, d), W.BF16)
+    return case, q, cu
+
+
+def check_prefill(got, ref, vmax, bf16_out):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), "non-finite output"
+    bound = 2.0 ** -9 * vmax + 1e-4 + (2.0 ** -8 * np.abs(ref) if bf16_out else 0.0)
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} elements out of bound (max err {err.max():.3g})"
+    return float(err.max())
+
+
+def run_case(pkv, case, q, cu, max_query=None):
+    dc = DevCase(case)
+    dc.write(pkv)  # the newest token of each sequence (its slot was poisoned)
+    kc, vc = oracle_after_write(case)
+    ref = P.prefill(q, kc, vc, case.block_tables, case.context_lens, cu, case.scale, W.BF16)
+    vmax = float(np.max(np.abs(out_to_f64_np(vc))))
+    mq = int(np.max(np.diff(cu))) if max_query is None else max_query
+    dq, dcu = to_dev(q), to_dev(cu)
+    for od in (torch.float32, None):
+        announce(case.name, "prefill out", od)
+        out = pkv.pa_prefill(dq, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, dcu, mq,
+                             case.max_context, case.scale, out_dtype=od)
+        check_prefill(out_to_f64(out), ref, vmax, bf16_out=od is None)
+    return dc
+
+
+def out_to_f64_np(a):
+    from oracle.numerics import bf16_bits_to_f64
+    a = np.asarray(a)
+    finite = bf16_bits_to_f64(a)
+    return np.where(np.isfinite(finite), finite, 0.0)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [(32, 8, 128, 16), (64, 8, 128, 16), (16, 8, 128, 32),
+                                         (8, 8, 128, 16), (16, 4, 64, 8), (32, 8, 64, 1)])
+def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
+    rng = np.random.default_rng(hq + d + bs)
+    lens = [1, 15, 16, 17, 100, 333, 64, 40]
+    nq = [1, 15, 16, 17, 100, 50, 1, 0]  # whole prompts, a chunk after cached keys, decode-like, empty
+    case, q, cu = make_prefill(int(rng.integers(1 << 20)), lens, nq, hq, hkv, d, bs)
+    run_case(gpu_lib, case, q, cu)
+
+
+def test_chunk_longer_than_context_gives_zero_rows(gpu_lib):
+    case, q, cu = make_prefill(31, [5, 40], [9, 40], 32, 8, 128, 16)
+    dc = run_case(gpu_lib, case, q, cu)
+    out = gpu_lib.pa_prefill(to_dev(q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, to_dev(cu), 40,
+                             case.max_context, case.scale, out_dtype=torch.float32).cpu().numpy()
+    assert np.all(out[:4] == 0.0)  # positions -4 .. -1
+
+
+def test_long_prompts_many_tiles(gpu_lib):
+    case, q, cu = make_prefill(41, [1500, 777, 2049], [1500, 300, 2049], 32, 8, 128, 16)
+    run_case(gpu_lib, case, q, cu)
+
+
+def test_placement_permutation_is_bitwise_invariant(gpu_lib):
+    case, q, cu = make_prefill(51, [300, 129], [300, 65], 32, 8, 128, 16, poison=False)
+    perm = np.random.default_rng(5).permutation(case.num_blocks)
+    k2, v2 = np.empty_like(case.k_cache), np.empty_like(case.v_cache)
+    k2[perm], v2[perm] = case.k_cache, case.v_cache
+    t2 = np.where(case.block_tables >= 0, perm[np.maximum(case.block_tables, 0)], -1).astype(np.int32)
+    outs = []
+    for kc, vc, tb in ((case.k_cache, case.v_cache, case.block_tables), (k2, v2, t2)):
+        outs.append(gpu_lib.pa_prefill(to_dev(q), to_dev(kc), to_dev(vc), to_dev(tb), to_dev(case.context_lens),
+                                       to_dev(cu), 300, case.max_context, case.scale, out_dtype=torch.float32))
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_argument_errors(gpu_lib):
+    case, q, cu = make_prefill(61, [20], [20], 32, 8, 128, 16, poison=False)
+    dc = DevCase(case)
+    f32 = torch.zeros((4, 4, 2, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(gpu_lib.PagedKVError):  # fp32 pools are not built
+        gpu_lib.pa_prefill(torch.zeros((20, 32, 128), dtype=torch.float32, device="cuda"), f32, f32,
+                           dc.block_tables, dc.context_lens, to_dev(cu), 20, 20, 1.0)
+    with pytest.raises(gpu_lib.PagedKVError):  # 12 / 8 query heads
+        gpu_lib.pa_prefill(to_dev(q)[:, :12].contiguous(), dc.k_cache, dc.v_cache, dc.block_tables,
+                           dc.context_lens, to_dev(cu), 20, 20, 1.0)
