@@ -73,6 +73,14 @@ WORKLOADS = {
     "tiny_f32": (lambda: W.c1_tiny_f32(), BALANCED),
 }
 DEFAULT_WORKLOAD = "llama3_8b_b64"
+# Prompt prefill (pa_write_kv of the chunk's tokens, then pa_prefill); reported
+# in TFLOP/s against the dense bf16 matrix-core peak.
+PREFILL_WORKLOADS = {
+    "prefill_llama3_8b": lambda: W.c6_prefill_llama8b(),
+    "prefill_chunked": lambda: W.c6_chunked_prefill(),
+}
+PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (causal QK and PV flops)"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", f)
                for f in ("pa_decode.hip", "pa_decode_gqa.hip", "pa_decode_common.h")]
@@ -87,7 +95,7 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
     p.add_argument("--partition", type=int, default=None,
                    help="decode partition_size (default: the workload's configuration)")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache decode calls (0: skip)")
@@ -218,6 +226,128 @@ def cpu_baseline(case, plan, budget_s):
             "tokens_per_s": round(done_tok / dt, 1), "seconds": round(dt, 2)}
 
 
+def prefill_flops(pc):
+    """Algorithmic flops of one pa_prefill call: for every (query, visible
+    key, query head), 2d for q.k and 2d for p.v."""
+    lens = pc.case.context_lens.astype(np.int64)
+    nq = np.diff(pc.cu_seqlens).astype(np.int64)
+    pairs = 0
+    for ctx, n in zip(lens, nq):
+        first = ctx - n  # position of the first query
+        # sum over i < n of (first + i + 1) visible keys, clipped at 0
+        pos = np.arange(n, dtype=np.int64) + first + 1
+        pairs += int(np.clip(pos, 0, None).sum())
+    return pairs * pc.case.num_q_heads * 4 * pc.case.head_dim
+
+
+def prefill_cpu_baseline(pc, budget_s):
+    """fp64 oracle rows (every head of a token) cycling over the chunk's
+    tokens until the budget is spent; TFLOP/s on the same flop count."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import prefill as P
+
+    c = pc.case
+    grp = c.num_q_heads // c.num_kv_heads
+    rows = [(s, i) for s in range(c.num_seqs) for i in range(int(pc.cu_seqlens[s + 1] - pc.cu_seqlens[s]))]
+    order = np.random.default_rng(0).permutation(len(rows))
+    flops, n = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        s, i = rows[order[n % len(rows)]]
+        ctx = int(c.context_lens[s])
+        nq = int(pc.cu_seqlens[s + 1] - pc.cu_seqlens[s])
+        pos = ctx - nq + i
+        for h in range(c.num_q_heads):
+            P.prefill_row(pc.q[pc.cu_seqlens[s] + i, h], c.k_cache, c.v_cache, c.block_tables[s], ctx, pos, c.scale,
+                          c.dtype, h // grp)
+        flops += max(pos + 1, 0) * c.num_q_heads * 4 * c.head_dim
+        n += 1
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle rows (all {c.num_q_heads} heads of a token), {n} tokens drawn at random "
+                      f"from the chunk, {dt:.1f} s wall", "seconds": round(dt, 2)}
+
+
+def prefill_main(args, torch, pkv, dev):
+    """One step: pa_write_kv of the chunk's tokens, then pa_prefill."""
+    log(f"workload {args.workload}: drawing inputs")
+    pc = PREFILL_WORKLOADS[args.workload]()
+    c = pc.case
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    k0, v0 = dev_t(c.k_cache), dev_t(c.v_cache)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.layers, 1) - 1)]
+    q, kn, vn, slots = dev_t(pc.q), dev_t(pc.k_new), dev_t(pc.v_new), dev_t(pc.slot_mapping)
+    tables, lens, cu = dev_t(c.block_tables), dev_t(c.context_lens), dev_t(pc.cu_seqlens)
+    out = torch.empty_like(q)
+    steps = []
+    for kc, vc in layers:
+        steps.append((pkv.prepare_write_kv(kn, vn, slots, kc, vc),
+                      pkv.prepare_prefill(q, kc, vc, tables, lens, cu, pc.max_query_len, c.max_context, c.scale,
+                                          out)))
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        for call in steps[i % len(steps)]:
+            call()
+    torch.cuda.synchronize()
+    log(f"timed {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for call in steps[i % len(steps)]:
+            call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        steps[i % len(steps)][1]()
+    e1.record()
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / 1e3 / args.steps
+    flops = prefill_flops(pc)
+    achieved = flops / avg / 1e12
+    elt = 2
+    write_bytes = pc.num_tokens * c.num_kv_heads * c.head_dim * elt * 2 * 2
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(flops / (wall / args.steps) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block placement)",
+        "config": {"workload": args.workload, "num_seqs": c.num_seqs, "num_q_heads": c.num_q_heads,
+                   "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "block_size": c.block_size,
+                   "query_tokens": pc.num_tokens, "context_len_mean": round(float(c.context_lens.mean()), 1),
+                   "context_len_max": int(c.context_lens.max()), "kv_pool_copies": len(layers)},
+        "pct_of_peak": round(100.0 * flops / (wall / args.steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+        "flops_per_step": flops,
+        "write_bytes_per_step": write_bytes,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "avg_launch_us": round(avg * 1e6, 2),
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = prefill_cpu_baseline(pc, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # --- main ------------------------------------------------------------------------------
 
 def main(argv=None):
@@ -240,6 +370,8 @@ def main(argv=None):
         return 2
     pkv.load()  # raises when the HIP library is missing: there is no other path
     dev = torch.device("cuda:0")
+    if args.workload in PREFILL_WORKLOADS:
+        return prefill_main(args, torch, pkv, dev)
     make, default_part = WORKLOADS[args.workload]
     partition = default_part if args.partition is None else args.partition
 

@@ -8,6 +8,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -31,18 +33,27 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libpagedkv)")
 
 
-def command(out):
-    srcs = [os.path.join(HERE, s) for s in SOURCES]
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-function",
-            # no packed fp32 instructions (v_pk_*_f32) anywhere in the device code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", os.path.join(HERE, "csrc"), *srcs, "-o", out]
+COMMON_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+                # no packed fp32 instructions (v_pk_*_f32) anywhere in the device code
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extra flags.  The prefill kernel keeps its matrix-core
+# accumulators in ordinary VGPRs: its online-softmax rescale and its use of
+# the scores would otherwise copy them out of and back into AGPRs.
+EXTRA_FLAGS = {
+    "csrc/pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def compile_command(src, obj):
+    return [hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", os.path.join(HERE, "csrc"),
+            "-c", os.path.join(HERE, src), "-o", obj]
+
+
+def link_command(objs, out):
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,6 +63,17 @@ def build(verbose=False):
         raise RuntimeError(f"libpagedkv build failed:\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose=False):
+    """Compile every source to an object (in parallel, in a temporary
+    directory), link libpagedkv.so next to this file."""
+    with tempfile.TemporaryDirectory(prefix="pagedkv_build_") as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+        tmp = LIB + ".tmp"
+        _run(link_command(objs, tmp), verbose)
     os.replace(tmp, LIB)
     return LIB
 

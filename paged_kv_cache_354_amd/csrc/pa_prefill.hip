@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "pa.h"
 #include "pa_decode_common.h"
@@ -50,7 +51,11 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;  // 4 wave64s
 constexpr int kKeys = 32;      // keys per tile
-constexpr int kVtRow = 40;     // bf16 per V^T row in LDS: 32 keys + 8 of padding (bank spread)
+constexpr int kVtWords = 17;   // 32-bit words per V^T row in LDS: 16 key pairs + 1 (bank spread)
+constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
+constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
+// s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
+constexpr int kWaitVmem = 0x0F70;
 
 struct PrefillArgs {
   const uint4 *q;               // [T][Hq][D]
@@ -76,7 +81,8 @@ struct PrefillArgs {
 template <int D>
 struct PrefillShared {
   uint4 k[2][kKeys][D / 8 + 1];        // K rows of the tile (double buffer), 16 B of padding per row
-  uint16_t vt[2][D][kVtRow];           // V^T of the tile
+  uint32_t vt[2][D][kVtWords];         // V^T of the tile: bf16 key pairs per 32-bit word
+  int32_t tbl[kTblLds];                // block ids of keys [0, kend)
 };
 
 template <int D, int G>
@@ -87,21 +93,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int C = D / 8;            // 16-byte chunks per row
   constexpr int KSTEPS = D / 32;
   constexpr int OB = D / 16;          // 16-channel blocks of the output
-  constexpr int NCH = kKeys * C / kThreads;  // staged chunks per thread and tile
-  static_assert(kKeys * C % kThreads == 0, "tile chunks must split evenly over the threads");
   __shared__ PrefillShared<D> sh;
 
-  // Work order: head group, KV head, query block (last first: causal blocks
-  // near the end see the most keys), sequence; contiguous ranges per XCD so
-  // that the blocks sharing a (sequence, KV head) share an L2.
+  // Work order: query block (last first: causal blocks near the end see the
+  // most keys), head group, KV head, sequence; contiguous ranges per XCD, so
+  // the workgroups an XCD runs together read the same (sequence, KV head)
+  // keys and values from its L2.
   const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
   int r = xcd_work_id(blockIdx.x, n_work);
+  const int qb = a.q_blocks - 1 - r % a.q_blocks;
+  r /= a.q_blocks;
   const int hg = r % HG;
   r /= HG;
   const int kvh = r % a.num_kv_heads;
-  r /= a.num_kv_heads;
-  const int qb = a.q_blocks - 1 - r % a.q_blocks;
-  const int s = r / a.q_blocks;
+  const int s = r / a.num_kv_heads;
 
   const int lo = a.cu_seqlens[s];
   const int n = a.cu_seqlens[s + 1] - lo;
@@ -144,39 +149,74 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const size_t block_rows = (size_t)a.num_kv_heads * a.block_size;
   const size_t head_rows = (size_t)kvh * a.block_size;
 
-  // Staging: thread tid moves chunks tid, tid + 256, ... of the tile's
-  // kKeys x C chunks; keys at or past kend are zeros (never visible).
-  uint4 kreg[NCH], vreg[NCH];
+  // The block ids of keys [0, kend), staged once when they fit.
+  const int nblk = (kend + a.block_size - 1) >> a.log2_bs;
+  const bool tbl_lds = nblk <= kTblLds;
+  if (tbl_lds)
+    for (int i = tid; i < nblk; i += kThreads) {
+      const int blk = trow[i];
+      sh.tbl[i] = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;  // stay inside the pool
+    }
+  __syncthreads();
+
+  // Staging: item i (thread tid, tid + 256, ...) moves 16-byte chunk ch of
+  // keys 2kp and 2kp + 1 (ch = i % C, kp = i / C), so that each load
+  // instruction reads whole rows; with D = 64 the last two waves have no
+  // item.  Loads are not predicated per lane, so that nothing serialises
+  // them: a key at or past kend reads key kend - 1 and is stored as zeros (it
+  // is never visible).
+  constexpr int ITEMS = kKeys / 2 * C;
+  constexpr int NCH = (ITEMS + kThreads - 1) / kThreads;
+  static_assert(ITEMS % 64 == 0, "items must cover whole waves");
+  uint4 kreg[NCH][2], vreg[NCH][2];
+
+  // The tile loop, with the block ids read from LDS (STAGED) or from HBM.
+  auto run = [&](auto staged_tag) {
+  constexpr bool STAGED = decltype(staged_tag)::value;
+  auto key_row = [&](int kk) -> size_t {
+    int blk;
+    if constexpr (STAGED) blk = sh.tbl[kk >> a.log2_bs];
+    else blk = max(0, min(trow[kk >> a.log2_bs], a.num_blocks - 1));
+    return (size_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
+  };
   auto load_tile = [&](int kt0) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int idx = tid + u * kThreads;
-      const int kk = kt0 + idx / C;
-      const int ch = idx % C;
-      if (kk < kend) {
-        int blk = trow[kk >> a.log2_bs];
-        blk = (unsigned)blk < (unsigned)a.num_blocks ? blk : 0;  // stay inside the pool
-        const size_t row = (size_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
-        kreg[u] = a.k_cache[row * C + ch];
-        vreg[u] = load_stream(a.v_cache + row * C + ch);
-      } else {
-        kreg[u] = make_uint4(0, 0, 0, 0);
-        vreg[u] = make_uint4(0, 0, 0, 0);
+      const int item = tid + u * kThreads;
+      if (item >= ITEMS) break;  // uniform per wave
+      const int ch = item % C;
+      const int kp = item / C;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kk = min(kt0 + 2 * kp + e, kend - 1);
+        const size_t row = key_row(kk);
+        kreg[u][e] = a.k_cache[row * C + ch];
+        vreg[u][e] = load_stream(a.v_cache + row * C + ch);
       }
     }
   };
-  auto store_tile = [&](int b) {
+  auto store_tile = [&](int b, int kt0) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int idx = tid + u * kThreads;
-      const int key = idx / C;
-      const int ch = idx % C;
-      sh.k[b][key][ch] = kreg[u];
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+      const int item = tid + u * kThreads;
+      if (item >= ITEMS) break;  // uniform per wave
+      const int ch = item % C;
+      const int kp = item / C;
+      uint4 kv[2], vv[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sh.vt[b][8 * ch + 2 * e][key] = (uint16_t)(w[e] & 0xffffu);
-        sh.vt[b][8 * ch + 2 * e + 1][key] = (uint16_t)(w[e] >> 16);
+      for (int e = 0; e < 2; ++e) {
+        const bool live = kt0 + 2 * kp + e < kend;
+        kv[e] = live ? kreg[u][e] : make_uint4(0, 0, 0, 0);
+        vv[e] = live ? vreg[u][e] : make_uint4(0, 0, 0, 0);
+        sh.k[b][2 * kp + e][ch] = kv[e];
+      }
+      // V^T: channel 8ch + c gets the word (key 2kp, key 2kp + 1)
+      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
+      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        sh.vt[b][8 * ch + 2 * c][kp] = (w0[c] & 0xffffu) | (w1[c] << 16);
+        sh.vt[b][8 * ch + 2 * c + 1][kp] = (w0[c] >> 16) | (w1[c] & 0xffff0000u);
       }
     }
   };
@@ -184,8 +224,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int ntiles = (kend + kKeys - 1) / kKeys;
   if (ntiles > 0) {
     load_tile(0);
-    store_tile(0);
+    store_tile(0, 0);
   }
+  // Nothing in flight from here on (the query loads included), so the waits
+  // in the loop only cover the next tile's loads.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int b = t & 1;
@@ -216,35 +259,43 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2_fast(m - mn);
-      m = mn;
+      // The reference max m moves only when a row's scores pass it by more
+      // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
+      // 2^kLazyMax, and the rescale of O^T (held in matrix-core registers)
+      // is rare after the first tiles.  The result does not depend on m.
+      if (__any(mx > m + kLazyMax)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = exp2_fast(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int j = 0; j < OB; ++j) o[j] *= alpha;
+      }
       f32x8_t p;
       float ps = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = exp2_fast(z[e] - mn);
+        p[e] = exp2_fast(z[e] - m);
         ps += p[e];
       }
-      l = fmaf(l, alpha, ps);
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int j = 0; j < OB; ++j) o[j] *= alpha;
-      }
+      l += ps;
       const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);
       // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
 #pragma unroll
       for (int j = 0; j < OB; ++j) {
-        const uint16_t *vr = &sh.vt[b][16 * j + nl][0];
-        const uint2 k_lo = *reinterpret_cast<const uint2 *>(vr + 4 * g);
-        const uint2 k_hi = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * g);
-        const uint4 av = make_uint4(k_lo.x, k_lo.y, k_hi.x, k_hi.y);
+        const uint32_t *vr = &sh.vt[b][16 * j + nl][0];  // key pairs
+        // keys 4g .. 4g + 3, then 16 + 4g .. 16 + 4g + 3 (rows are 17 words:
+        // 4-byte reads only)
+        const uint4 av = make_uint4(vr[2 * g], vr[2 * g + 1], vr[8 + 2 * g], vr[9 + 2 * g]);
         o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[j], 0, 0, 0);
       }
     }
-    if (t + 1 < ntiles) store_tile(b ^ 1);
+    if (t + 1 < ntiles) store_tile(b ^ 1, kt0 + kKeys);
     __syncthreads();
   }
+  };
+  if (tbl_lds) run(std::true_type{});
+  else run(std::false_type{});
 
   // Row sums over the row's 4 lanes; normalised output.
   l += __shfl_xor(l, 16, 64);

@@ -115,3 +115,34 @@ def test_argument_errors(gpu_lib):
     with pytest.raises(gpu_lib.PagedKVError):  # 12 / 8 query heads
         gpu_lib.pa_prefill(to_dev(q)[:, :12].contiguous(), dc.k_cache, dc.v_cache, dc.block_tables,
                            dc.context_lens, to_dev(cu), 20, 20, 1.0)
+
+
+@pytest.mark.parametrize("name", ["prefill_llama3_8b", "prefill_chunked"])
+def test_full_size_sampled(gpu_lib, name):
+    """The benchmarked prefill step (store the chunk's tokens, then attend) at
+    full size; sampled rows against the oracle (each row is one query's
+    softmax over its visible keys)."""
+    pc = W.c6_prefill_llama8b() if name == "prefill_llama3_8b" else W.c6_chunked_prefill()
+    c = pc.case
+    announce("prefill full", name)
+    dc = DevCase(c)
+    gpu_lib.pa_write_kv(to_dev(pc.k_new), to_dev(pc.v_new), to_dev(pc.slot_mapping), dc.k_cache, dc.v_cache)
+    out = gpu_lib.pa_prefill(to_dev(pc.q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                             to_dev(pc.cu_seqlens), pc.max_query_len, c.max_context, c.scale,
+                             out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    del dc
+    torch.cuda.empty_cache()
+    from oracle import kvcache as KV
+    kc, vc = KV.write_kv(c.k_cache, c.v_cache, pc.k_new, pc.v_new, pc.slot_mapping, c.block_size)
+    vmax = float(np.max(np.abs(out_to_f64_np(vc))))
+    grp = c.num_q_heads // c.num_kv_heads
+    rng = np.random.default_rng(21)
+    picks = rng.integers(0, pc.num_tokens, 40)
+    seq_of = np.searchsorted(pc.cu_seqlens, picks, side="right") - 1
+    for row, s in zip(picks, seq_of):
+        n = int(pc.cu_seqlens[s + 1] - pc.cu_seqlens[s])
+        pos = int(c.context_lens[s]) - n + int(row - pc.cu_seqlens[s])
+        for h in (0, int(rng.integers(c.num_q_heads))):
+            ref = P.prefill_row(pc.q[row, h], kc, vc, c.block_tables[s], c.context_lens[s], pos, c.scale, W.BF16,
+                                h // grp)
+            check_prefill(out[row, h], ref, vmax, bf16_out=False)

@@ -244,6 +244,81 @@ def c5_mha_sweep(seed=5, block_size=16, num_seqs=256, **kw):
                      num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=block_size, **kw)
 
 
+# --- prompt prefill -------------------------------------------------------------
+
+@dataclass
+class PrefillCase:
+    """A batch of prompt chunks to prefill through the paged pools.
+
+    ``case`` carries the pools, tables, context lengths and scale (its
+    single-token q / new rows are not used).  Sequence s's chunk is its last
+    ``n_s`` positions: queries ``q[cu_seqlens[s]:cu_seqlens[s+1]]`` and the
+    chunk tokens' keys / values ``k_new, v_new`` (same rows), to be stored at
+    ``slot_mapping`` (the table's slots of those positions) before the
+    attention.  Drawn after the case, from a second stream seeded
+    ``seed + 1``: chunk lengths (when drawn), q, K rows, V rows.
+    """
+
+    case: "DecodeCase"
+    q: np.ndarray             # [T][Hq][d]
+    cu_seqlens: np.ndarray    # int32 [B + 1]
+    k_new: np.ndarray         # [T][Hkv][d]
+    v_new: np.ndarray
+    slot_mapping: np.ndarray  # int64 [T]
+
+    @property
+    def num_tokens(self):
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def max_query_len(self):
+        return int(np.max(np.diff(self.cu_seqlens))) if len(self.cu_seqlens) > 1 else 0
+
+
+def make_prefill(name, *, seed, context_lens, chunk_lens=None, num_q_heads, num_kv_heads, head_dim,
+                 block_size, dtype=BF16, **kw):
+    """Prefill case: ``chunk_lens`` None means whole prompts (n_s = ctx_s)."""
+    case = make_case(name, seed=seed, dtype=dtype, context_lens=context_lens, num_q_heads=num_q_heads,
+                     num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size, **kw)
+    rng = np.random.default_rng(seed + 1)
+    lens = case.context_lens.astype(np.int64)
+    if chunk_lens is None:
+        nq = lens.copy()
+    elif callable(chunk_lens):
+        nq = np.minimum(np.asarray(chunk_lens(rng), dtype=np.int64), lens)
+    else:
+        nq = np.asarray(chunk_lens, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    t = int(cu[-1])
+    q = normal(rng, (t, num_q_heads, head_dim), dtype)
+    k_new = normal(rng, (t, num_kv_heads, head_dim), dtype)
+    v_new = normal(rng, (t, num_kv_heads, head_dim), dtype)
+    slots = np.full(t, -1, dtype=np.int64)
+    for s in range(len(lens)):
+        for i in range(int(nq[s])):
+            pos = int(lens[s] - nq[s] + i)
+            if pos >= 0:
+                slots[cu[s] + i] = int(case.block_tables[s, pos // block_size]) * block_size + pos % block_size
+    return PrefillCase(case=case, q=q, cu_seqlens=cu, k_new=k_new, v_new=v_new, slot_mapping=slots)
+
+
+def c6_prefill_llama8b(seed=6, num_seqs=8, lo=512, hi=4096):
+    """Llama-3-8B-shaped prompt prefill, bf16: 8 whole prompts of U{512..4096} tokens,
+    32 q / 8 KV heads, d 128, bs 16."""
+    return make_prefill("prefill_llama3_8b", seed=seed,
+                        context_lens=lambda r: r.integers(lo, hi, size=num_seqs, endpoint=True),
+                        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16)
+
+
+def c6_chunked_prefill(seed=7, num_seqs=16, lo=1024, hi=8192, chunk=512):
+    """Chunked prefill after a cached context, bf16: 16 sequences of U{1024..8192} keys whose last
+    512 positions are the new chunk, 32 q / 8 KV heads, d 128, bs 16."""
+    return make_prefill("prefill_chunked", seed=seed,
+                        context_lens=lambda r: r.integers(lo, hi, size=num_seqs, endpoint=True),
+                        chunk_lens=lambda r: np.full(num_seqs, chunk),
+                        num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16)
+
+
 # --- shared-prefix copy-on-write workload -------------------------------------
 
 @dataclass
