@@ -125,6 +125,28 @@ pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cache_t *cache
                            const int64_t *src_dst_pairs, int32_t num_pairs, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_swap_blocks -- copy whole blocks between two pools, typically a device
+ * pool and a swap pool in pinned host memory (in either direction).
+ * (foundry PagedAttention page, How it works and Trade-offs: a preempted
+ * sequence's blocks can be swapped out to CPU memory and back in.)
+ *
+ *   src_k, src_v / dst_k, dst_v  pools described by *src_cache / *dst_cache
+ *                 (the same block shape and dtype; num_blocks may differ).
+ *                 Device memory, or host memory the device can address
+ *                 (hipHostMalloc, e.g. torch pin_memory): the kernel reads
+ *                 and writes it directly.  16-byte aligned.
+ *   src_dst_pairs device-addressable int64 [num_pairs][2]: block src of the
+ *                 source pools goes to block dst of the destination pools,
+ *                 every KV head and slot, K and V.  Pairs naming a block
+ *                 outside its pool are skipped.
+ * Preconditions: distinct destinations; source and destination pools do not
+ * overlap.  Bytes are copied unchanged.  num_pairs == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_swap_blocks(const void *src_k, const void *src_v, const pa_cache_t *src_cache,
+                           void *dst_k, void *dst_v, const pa_cache_t *dst_cache,
+                           const int64_t *src_dst_pairs, int32_t num_pairs, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pa_decode -- single-query paged decode attention.
  * (foundry PagedAttention page, "How it works": the attention kernel reads
  * KV through the block table, gathering scattered blocks, so non-contiguous
@@ -297,13 +319,41 @@ pa_status_t pa_seq_free(pa_pool *pool, int64_t seq);
 pa_status_t pa_seq_slots(const pa_pool *pool, int64_t seq, int32_t start, int32_t count,
                          int64_t *slots);
 /* Table row of seq into host row[max_blocks] (padded with -1), plus its block
- * count and length.  PA_EINVAL if the row does not fit. */
+ * count and length (host swap block ids while seq is swapped out).
+ * PA_EINVAL if the row does not fit. */
 pa_status_t pa_seq_table(const pa_pool *pool, int64_t seq, int32_t *row, int32_t max_blocks,
                          int32_t *num_blocks, int32_t *len);
 /* Tables and lengths of seqs[0..n) into host tables[n][max_blocks] (padded
  * with -1) and context_lens[n], ready to upload for pa_decode. */
 pa_status_t pa_pool_tables(const pa_pool *pool, const int64_t *seqs, int32_t n, int32_t *tables,
                            int32_t max_blocks, int32_t *context_lens);
+
+/* Swap space (foundry page, How it works and Trade-offs: under memory
+ * pressure a sequence is preempted and its blocks can move to CPU memory and
+ * back).  The pool can own a second stack of num_host_blocks host swap
+ * blocks, handed out in host_free_order (NULL: 0, 1, ...), LIFO afterwards;
+ * the caller keeps the swap pools themselves (pa_swap_blocks moves the data).
+ * A swapped-out sequence may only be swapped in, inspected (pa_seq_table,
+ * pa_seq_is_swapped) or freed; other calls on it return PA_ESTATE, and so do
+ * pa_seq_slots / pa_pool_tables.  Every call succeeds or changes nothing. */
+/* Set up or replace the swap space; PA_ESTATE while a sequence is swapped
+ * out. */
+pa_status_t pa_pool_set_swap_space(pa_pool *pool, int32_t num_host_blocks, const int32_t *host_free_order);
+int32_t pa_pool_num_free_host(const pa_pool *pool);
+/* Free host blocks in hand-out order into out[cap]; *n = their count. */
+pa_status_t pa_pool_host_free_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n);
+/* 1 swapped out, 0 resident, -1 unknown sequence (or NULL pool). */
+int32_t pa_seq_is_swapped(const pa_pool *pool, int64_t seq);
+/* Swap seq out: each logical block, in order, gets a host block h; the pair
+ * (device block, h) is written to pairs[i][2] (cap pairs of room) and the
+ * device block loses one reference (it returns to the free pool unless
+ * another sequence shares it).  *num_pairs = blocks of seq.  PA_ENOMEM when
+ * the swap space has too few free blocks. */
+pa_status_t pa_seq_swap_out(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs);
+/* Swap seq back in: each host block, in logical order, gets a fresh device
+ * block b; pairs[i] = (host block, b); the host blocks return to the swap
+ * space.  PA_ENOMEM when the free pool is too small. */
+pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs);
 
 #ifdef __cplusplus
 }

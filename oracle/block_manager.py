@@ -29,6 +29,16 @@ Readings where the pages are silent (the same contract the C library states):
 * every failing call leaves the whole state unchanged;
 * a batch append checks every sequence id before taking any block (an
   unknown id is a state error even when the pool is also short).
+
+Swap (foundry page, *How it works* and *Trade-offs*: when the pool runs dry a
+scheduler preempts, and a preempted sequence's blocks can be swapped out to
+CPU memory and brought back).  Readings: the host swap space is a second
+stack of its own blocks; swapping out gives every logical block of the
+sequence its own host block, in logical order, and drops one reference to
+the device block (which returns to the free pool only if no other sequence
+shares it); swapping in takes a device block per host block, in logical
+order, and returns the host blocks; a swapped-out sequence can only be
+swapped in, inspected or released.
 """
 
 import copy
@@ -55,6 +65,8 @@ class BlockManagerModel:
         self.refcount = [0] * num_blocks
         self.tables = {}
         self.lens = {}
+        self.host_free = []   # host swap blocks, top of stack = end of list
+        self.swapped = set()  # sequences whose table names host blocks
 
     # -- helpers ---------------------------------------------------------
     def _take(self):
@@ -72,13 +84,16 @@ class BlockManagerModel:
     def _need(self, seq):
         if seq not in self.tables:
             raise StateError(f"unknown sequence {seq}")
+        if seq in self.swapped:
+            raise StateError(f"sequence {seq} is swapped out")
 
     def _atomic(self, fn):
-        saved = (list(self.free), list(self.refcount), copy.deepcopy(self.tables), dict(self.lens))
+        saved = (list(self.free), list(self.refcount), copy.deepcopy(self.tables), dict(self.lens),
+                 list(self.host_free), set(self.swapped))
         try:
             return fn()
         except Exception:
-            self.free, self.refcount, self.tables, self.lens = saved
+            self.free, self.refcount, self.tables, self.lens, self.host_free, self.swapped = saved
             raise
 
     # -- operations -------------------------------------------------------
@@ -162,11 +177,66 @@ class BlockManagerModel:
         return self._atomic(run)
 
     def release(self, seq):
-        """Return every block of ``seq`` to the pool (count drops by one each)."""
+        """Return every block of ``seq`` to its pool (device: count drops by
+        one each; host swap blocks of a swapped-out sequence: freed)."""
+        if seq in self.swapped:
+            self.swapped.remove(seq)
+            self.host_free.extend(self.tables.pop(seq))
+            del self.lens[seq]
+            return
         self._need(seq)
         for blk in self.tables.pop(seq):
             self._release(blk)
         del self.lens[seq]
+
+    # -- swap ---------------------------------------------------------------
+    def set_swap_space(self, num_host_blocks, host_free_order=None):
+        """A host swap space of ``num_host_blocks`` blocks (replaces the old
+        one; not while a sequence is swapped out)."""
+        if self.swapped:
+            raise StateError("sequences are swapped out")
+        order = list(range(num_host_blocks)) if host_free_order is None else [int(h) for h in host_free_order]
+        if sorted(order) != list(range(num_host_blocks)):
+            raise StateError("host_free_order must be a permutation")
+        self.host_free = list(reversed(order))
+
+    def swap_out(self, seq):
+        """Move ``seq`` to host blocks; returns the (device, host) copies to do."""
+        self._need(seq)
+        table = self.tables[seq]
+        if len(table) > len(self.host_free):
+            raise PoolExhausted()
+        pairs = []
+        for lb, blk in enumerate(table):
+            h = self.host_free.pop()
+            pairs.append((blk, h))
+            table[lb] = h
+            self._release(blk)
+        self.swapped.add(seq)
+        return pairs
+
+    def swap_in(self, seq):
+        """Bring ``seq`` back to device blocks; returns the (host, device) copies."""
+        if seq not in self.tables:
+            raise StateError(f"unknown sequence {seq}")
+        if seq not in self.swapped:
+            raise StateError(f"sequence {seq} is not swapped out")
+        table = self.tables[seq]
+        if len(table) > len(self.free):
+            raise PoolExhausted()
+        pairs = []
+        for lb, h in enumerate(table):
+            blk = self._take()
+            pairs.append((h, blk))
+            table[lb] = blk
+            self.host_free.append(h)
+        self.swapped.remove(seq)
+        return pairs
+
+    def is_swapped(self, seq):
+        if seq not in self.tables:
+            raise StateError(f"unknown sequence {seq}")
+        return seq in self.swapped
 
     def slots(self, seq, start, count):
         """Slots of logical positions ``start .. start+count-1`` of ``seq``."""
@@ -185,9 +255,12 @@ class BlockManagerModel:
         return len(self.free)
 
     def table(self, seq):
-        self._need(seq)
+        """Block ids of ``seq`` (host swap blocks while it is swapped out)."""
+        if seq not in self.tables:
+            raise StateError(f"unknown sequence {seq}")
         return list(self.tables[seq])
 
     def length(self, seq):
-        self._need(seq)
+        if seq not in self.tables:
+            raise StateError(f"unknown sequence {seq}")
         return self.lens[seq]

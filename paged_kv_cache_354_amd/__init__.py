@@ -9,6 +9,8 @@ The functions carry the C names declared in ``include/pa.h``:
 
 * ``pa_write_kv``     -- new tokens' K/V into their slots
 * ``pa_copy_blocks``  -- whole-block copies for copy-on-write
+* ``pa_swap_blocks``  -- whole-block copies between a device pool and a pinned
+  host swap pool
 * ``pa_decode``       -- paged single-query decode attention
 * ``pa_decode_write`` -- ``pa_write_kv`` then ``pa_decode`` in one call
 * ``pa_prefill``      -- causal paged attention of a chunk of new queries
@@ -88,6 +90,14 @@ _SIGS = {
     "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _P64]),
     "pa_seq_table": (_i32, [_vp, _i64, _P32, _i32, _P32, _P32]),
     "pa_pool_tables": (_i32, [_vp, _P64, _i32, _P32, _i32, _P32]),
+    "pa_swap_blocks": (_i32, [_vp, _vp, ctypes.POINTER(PaCache), _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32,
+                              _vp]),
+    "pa_pool_set_swap_space": (_i32, [_vp, _i32, _P32]),
+    "pa_pool_num_free_host": (_i32, [_vp]),
+    "pa_pool_host_free_list": (_i32, [_vp, _P32, _i32, _P32]),
+    "pa_seq_is_swapped": (_i32, [_vp, _i64]),
+    "pa_seq_swap_out": (_i32, [_vp, _i64, _P64, _i32, _P32]),
+    "pa_seq_swap_in": (_i32, [_vp, _i64, _P64, _i32, _P32]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -194,6 +204,33 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     _check(load().pa_copy_blocks(kp, vp, ctypes.byref(desc),
                                  _dev(src_dst_pairs, "src_dst_pairs", torch.int64, (n, 2)), n,
                                  _stream(stream)))
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, stream=None):
+    """Copy block ``src`` of the source pools to ``dst`` of the destination
+    pools for each int64 (src, dst) row; either side may be a pinned host
+    tensor (``pin_memory``) or a device tensor; ``src_dst_pairs`` must be
+    device-addressable (a device tensor, or pinned host memory)."""
+    torch = _torch()
+    sd, dd = cache_desc(src_k), cache_desc(dst_k)
+    n = int(src_dst_pairs.shape[0])
+    if n == 0:
+        return
+
+    def ptr(t, name, like):
+        if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+            raise TypeError(f"{name} must be a GPU tensor or a pinned host tensor")
+        if not t.is_contiguous() or t.dtype != like.dtype or tuple(t.shape) != tuple(like.shape):
+            raise ValueError(f"{name} must be contiguous, of the same dtype and shape as its pair")
+        return ctypes.c_void_p(t.data_ptr())
+
+    pairs = src_dst_pairs
+    if pairs.dtype != torch.int64 or tuple(pairs.shape) != (n, 2) or not pairs.is_contiguous() or \
+            not (pairs.is_cuda or pairs.is_pinned()):
+        raise ValueError("src_dst_pairs must be a contiguous int64 [n][2] GPU or pinned tensor")
+    _check(load().pa_swap_blocks(ptr(src_k, "src_k", src_k), ptr(src_v, "src_v", src_k), ctypes.byref(sd),
+                                 ptr(dst_k, "dst_k", dst_k), ptr(dst_v, "dst_v", dst_k), ctypes.byref(dd),
+                                 ctypes.c_void_p(pairs.data_ptr()), n, _stream(stream)))
 
 
 def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
@@ -358,6 +395,57 @@ def pa_pool_free_list(pool):
     return out[:got.value]
 
 
+def pa_pool_set_swap_space(pool, num_host_blocks, host_free_order=None):
+    order = None
+    if host_free_order is not None:
+        order = np.ascontiguousarray(host_free_order, dtype=np.int32)
+        if order.shape != (num_host_blocks,):
+            raise ValueError("host_free_order must have num_host_blocks entries")
+    _check(load().pa_pool_set_swap_space(pool, num_host_blocks,
+                                         _np_ptr(order, ctypes.c_int32) if order is not None else None))
+
+
+def pa_pool_num_free_host(pool):
+    return int(load().pa_pool_num_free_host(pool))
+
+
+def pa_pool_host_free_list(pool):
+    n = pa_pool_num_free_host(pool)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(load().pa_pool_host_free_list(pool, _np_ptr(out, ctypes.c_int32), n, ctypes.byref(got)))
+    return out[:got.value]
+
+
+def pa_seq_is_swapped(pool, seq):
+    r = int(load().pa_seq_is_swapped(pool, seq))
+    if r < 0:
+        raise PoolStateError(PA_ESTATE, f"unknown sequence {seq}")
+    return bool(r)
+
+
+def _swap(fn, pool, seq):
+    nb = ctypes.c_int32()
+    lib = load()
+    st = lib.pa_seq_table(pool, seq, None, 0, ctypes.byref(nb), ctypes.byref(ctypes.c_int32()))
+    if st not in (PA_OK, PA_EINVAL):
+        _check(st)
+    pairs = np.empty((max(nb.value, 1), 2), dtype=np.int64)
+    got = ctypes.c_int32()
+    _check(getattr(lib, fn)(pool, seq, _np_ptr(pairs, ctypes.c_int64), nb.value, ctypes.byref(got)))
+    return pairs[:got.value]
+
+
+def pa_seq_swap_out(pool, seq):
+    """Swap ``seq`` out; returns int64 [n][2] (device block, host block) copies to do."""
+    return _swap("pa_seq_swap_out", pool, seq)
+
+
+def pa_seq_swap_in(pool, seq):
+    """Swap ``seq`` in; returns int64 [n][2] (host block, device block) copies to do."""
+    return _swap("pa_seq_swap_in", pool, seq)
+
+
 def pa_seq_create(pool, seq, num_tokens):
     _check(load().pa_seq_create(pool, seq, num_tokens))
 
@@ -493,6 +581,24 @@ class BlockPool:
 
     def tables(self, seqs, max_blocks, tables=None, context_lens=None):
         return pa_pool_tables(self.handle, seqs, max_blocks, tables, context_lens)
+
+    def set_swap_space(self, num_host_blocks, host_free_order=None):
+        pa_pool_set_swap_space(self.handle, num_host_blocks, host_free_order)
+
+    def swap_out(self, seq):
+        return pa_seq_swap_out(self.handle, seq)
+
+    def swap_in(self, seq):
+        return pa_seq_swap_in(self.handle, seq)
+
+    def is_swapped(self, seq):
+        return pa_seq_is_swapped(self.handle, seq)
+
+    def num_free_host(self):
+        return pa_pool_num_free_host(self.handle)
+
+    def host_free_order(self):
+        return pa_pool_host_free_list(self.handle)
 
 
 # --- prepared calls ----------------------------------------------------------------

@@ -18,6 +18,16 @@
 // free_order so that free_order[0] is handed out first; release walks a table
 // in logical order; the writer of a shared block gets the private copy.  Every
 // call either succeeds or leaves the pool untouched.
+//
+// Swap (foundry page, How it works and Trade-offs: when the pool runs dry a
+// scheduler preempts, and a preempted sequence's blocks can be swapped out to
+// CPU memory and back in): an optional host swap space of its own blocks, a
+// second LIFO stack.  Swapping a sequence out gives each of its logical
+// blocks its own host block (in logical order) and drops one reference to
+// the device block, which returns to the free pool when no other sequence
+// shares it; swapping in takes a device block per host block and returns the
+// host blocks.  A swapped-out sequence can only be swapped in, inspected or
+// freed.
 
 #include <cstdint>
 #include <cstring>
@@ -31,8 +41,9 @@
 namespace {
 
 struct Seq {
-  std::vector<int32_t> table;
+  std::vector<int32_t> table;  // device block ids, or host swap blocks while swapped out
   int64_t len = 0;
+  bool swapped = false;
 };
 
 }  // namespace
@@ -43,6 +54,9 @@ struct pa_pool {
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
+  int32_t num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // host swap blocks; back() is handed out next
+  int32_t swapped_seqs = 0;
 
   int32_t take() {
     int32_t b = free_stack.back();
@@ -79,6 +93,17 @@ struct pa_pool {
 };
 
 using pa::fail;
+
+namespace {
+// A resident (not swapped-out) sequence, or an error.
+pa_status_t resident(pa_pool *pool, int64_t seq, const char *fn, Seq **out) {
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "%s: unknown sequence %lld", fn, (long long)seq);
+  if (it->second.swapped) return fail(PA_ESTATE, "%s: sequence %lld is swapped out", fn, (long long)seq);
+  *out = &it->second;
+  return PA_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -149,10 +174,10 @@ pa_status_t pa_seq_create(pa_pool *pool, int64_t seq, int32_t num_tokens) {
 
 pa_status_t pa_seq_fork(pa_pool *pool, int64_t parent, int64_t child) {
   if (!pool) return fail(PA_EINVAL, "pa_seq_fork: pool is NULL");
-  auto it = pool->seqs.find(parent);
-  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_fork: unknown sequence %lld", (long long)parent);
+  Seq *par;
+  if (pa_status_t st = resident(pool, parent, "pa_seq_fork", &par)) return st;
   if (pool->seqs.count(child)) return fail(PA_ESTATE, "pa_seq_fork: sequence %lld exists", (long long)child);
-  Seq s = it->second;
+  Seq s = *par;
   for (int32_t b : s.table) pool->refcount[b] += 1;
   pool->seqs.emplace(child, std::move(s));
   return PA_OK;
@@ -160,11 +185,11 @@ pa_status_t pa_seq_fork(pa_pool *pool, int64_t parent, int64_t child) {
 
 pa_status_t pa_seq_append(pa_pool *pool, int64_t seq, int64_t *slot, int64_t cow_pair[2]) {
   if (!pool || !slot || !cow_pair) return fail(PA_EINVAL, "pa_seq_append: NULL argument");
-  auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_append: unknown sequence %lld", (long long)seq);
-  if (pool->append_need(it->second) > (int32_t)pool->free_stack.size())
+  Seq *sq;
+  if (pa_status_t st = resident(pool, seq, "pa_seq_append", &sq)) return st;
+  if (pool->append_need(*sq) > (int32_t)pool->free_stack.size())
     return fail(PA_ENOMEM, "pa_seq_append: free pool is empty");
-  pool->append(it->second, slot, cow_pair);
+  pool->append(*sq, slot, cow_pair);
   return PA_OK;
 }
 
@@ -174,12 +199,8 @@ pa_status_t pa_seq_append_batch(pa_pool *pool, const int64_t *seqs, int32_t n, i
     return fail(PA_EINVAL, "pa_seq_append_batch: bad argument");
   *num_pairs = 0;
   std::vector<Seq *> refs(n);
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = pool->seqs.find(seqs[i]);
-    if (it == pool->seqs.end())
-      return fail(PA_ESTATE, "pa_seq_append_batch: unknown sequence %lld", (long long)seqs[i]);
-    refs[i] = &it->second;
-  }
+  for (int32_t i = 0; i < n; ++i)
+    if (pa_status_t st = resident(pool, seqs[i], "pa_seq_append_batch", &refs[i])) return st;
   // Dry run on counts only, so that a shortage is found before anything
   // changes.  A repeated sequence sees its own earlier appends.
   {
@@ -225,9 +246,9 @@ pa_status_t pa_seq_append_batch(pa_pool *pool, const int64_t *seqs, int32_t n, i
 pa_status_t pa_seq_cow(pa_pool *pool, int64_t seq, int32_t logical_block, int64_t pair[2]) {
   if (!pool || !pair) return fail(PA_EINVAL, "pa_seq_cow: NULL argument");
   pair[0] = pair[1] = -1;
-  auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_cow: unknown sequence %lld", (long long)seq);
-  Seq &s = it->second;
+  Seq *sq;
+  if (pa_status_t st = resident(pool, seq, "pa_seq_cow", &sq)) return st;
+  Seq &s = *sq;
   if (logical_block < 0 || logical_block >= (int32_t)s.table.size())
     return fail(PA_ESTATE, "pa_seq_cow: logical block %d outside [0, %zu)", logical_block,
                 s.table.size());
@@ -246,7 +267,12 @@ pa_status_t pa_seq_free(pa_pool *pool, int64_t seq) {
   if (!pool) return fail(PA_EINVAL, "pa_seq_free: pool is NULL");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_free: unknown sequence %lld", (long long)seq);
-  for (int32_t b : it->second.table) pool->release(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.table) pool->host_free.push_back(h);
+    pool->swapped_seqs -= 1;
+  } else {
+    for (int32_t b : it->second.table) pool->release(b);
+  }
   pool->seqs.erase(it);
   return PA_OK;
 }
@@ -254,9 +280,9 @@ pa_status_t pa_seq_free(pa_pool *pool, int64_t seq) {
 pa_status_t pa_seq_slots(const pa_pool *pool, int64_t seq, int32_t start, int32_t count,
                          int64_t *slots) {
   if (!pool || (count > 0 && !slots)) return fail(PA_EINVAL, "pa_seq_slots: NULL argument");
-  auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_slots: unknown sequence %lld", (long long)seq);
-  const Seq &s = it->second;
+  Seq *sq;
+  if (pa_status_t st = resident(const_cast<pa_pool *>(pool), seq, "pa_seq_slots", &sq)) return st;
+  const Seq &s = *sq;
   if (start < 0 || count < 0 || (int64_t)start + count > s.len)
     return fail(PA_ESTATE, "pa_seq_slots: positions [%d, %d) outside length %lld", start,
                 start + count, (long long)s.len);
@@ -286,9 +312,9 @@ pa_status_t pa_pool_tables(const pa_pool *pool, const int64_t *seqs, int32_t n, 
   if (!pool || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !tables || !context_lens)))
     return fail(PA_EINVAL, "pa_pool_tables: bad argument");
   for (int32_t i = 0; i < n; ++i) {
+    Seq *sq;
+    if (pa_status_t st = resident(const_cast<pa_pool *>(pool), seqs[i], "pa_pool_tables", &sq)) return st;
     auto it = pool->seqs.find(seqs[i]);
-    if (it == pool->seqs.end())
-      return fail(PA_ESTATE, "pa_pool_tables: unknown sequence %lld", (long long)seqs[i]);
     if ((int32_t)it->second.table.size() > max_blocks)
       return fail(PA_EINVAL, "pa_pool_tables: sequence %lld has %zu blocks > %d", (long long)seqs[i],
                   it->second.table.size(), max_blocks);
@@ -301,6 +327,96 @@ pa_status_t pa_pool_tables(const pa_pool *pool, const int64_t *seqs, int32_t n, 
     for (int32_t j = nb; j < max_blocks; ++j) row[j] = -1;
     context_lens[i] = (int32_t)s.len;
   }
+  return PA_OK;
+}
+
+pa_status_t pa_pool_set_swap_space(pa_pool *pool, int32_t num_host_blocks, const int32_t *host_free_order) {
+  if (!pool) return fail(PA_EINVAL, "pa_pool_set_swap_space: pool is NULL");
+  if (num_host_blocks < 0)
+    return fail(PA_EINVAL, "pa_pool_set_swap_space: num_host_blocks=%d < 0", num_host_blocks);
+  if (pool->swapped_seqs > 0)
+    return fail(PA_ESTATE, "pa_pool_set_swap_space: %d sequences are swapped out", pool->swapped_seqs);
+  std::vector<int32_t> stack(num_host_blocks);
+  std::vector<char> seen(num_host_blocks, 0);
+  for (int32_t i = 0; i < num_host_blocks; ++i) {
+    int32_t h = host_free_order ? host_free_order[i] : i;
+    if (h < 0 || h >= num_host_blocks || seen[h])
+      return fail(PA_EINVAL, "pa_pool_set_swap_space: host_free_order is not a permutation (entry %d = %d)", i,
+                  h);
+    seen[h] = 1;
+    stack[num_host_blocks - 1 - i] = h;
+  }
+  pool->num_host_blocks = num_host_blocks;
+  pool->host_free.swap(stack);
+  return PA_OK;
+}
+
+int32_t pa_pool_num_free_host(const pa_pool *pool) { return pool ? (int32_t)pool->host_free.size() : -1; }
+
+pa_status_t pa_pool_host_free_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n) {
+  if (!pool || !n) return fail(PA_EINVAL, "pa_pool_host_free_list: NULL argument");
+  int32_t total = (int32_t)pool->host_free.size();
+  *n = total;
+  if (total > cap || (total > 0 && !out))
+    return fail(PA_EINVAL, "pa_pool_host_free_list: %d free host blocks do not fit in %d", total, cap);
+  for (int32_t i = 0; i < total; ++i) out[i] = pool->host_free[total - 1 - i];
+  return PA_OK;
+}
+
+int32_t pa_seq_is_swapped(const pa_pool *pool, int64_t seq) {
+  if (!pool) return -1;
+  auto it = pool->seqs.find(seq);
+  return it == pool->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+pa_status_t pa_seq_swap_out(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs) {
+  if (!pool || !num_pairs) return fail(PA_EINVAL, "pa_seq_swap_out: NULL argument");
+  *num_pairs = 0;
+  Seq *sq;
+  if (pa_status_t st = resident(pool, seq, "pa_seq_swap_out", &sq)) return st;
+  const int32_t nb = (int32_t)sq->table.size();
+  if (nb > cap || (nb > 0 && !pairs))
+    return fail(PA_EINVAL, "pa_seq_swap_out: %d pairs do not fit in %d", nb, cap);
+  if (nb > (int32_t)pool->host_free.size())
+    return fail(PA_ENOMEM, "pa_seq_swap_out: %d host blocks needed, %zu free", nb, pool->host_free.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t b = sq->table[i];
+    const int32_t h = pool->host_free.back();
+    pool->host_free.pop_back();
+    pairs[2 * i] = b;
+    pairs[2 * i + 1] = h;
+    sq->table[i] = h;
+    pool->release(b);
+  }
+  sq->swapped = true;
+  pool->swapped_seqs += 1;
+  *num_pairs = nb;
+  return PA_OK;
+}
+
+pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs) {
+  if (!pool || !num_pairs) return fail(PA_EINVAL, "pa_seq_swap_in: NULL argument");
+  *num_pairs = 0;
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) return fail(PA_ESTATE, "pa_seq_swap_in: unknown sequence %lld", (long long)seq);
+  Seq &s = it->second;
+  if (!s.swapped) return fail(PA_ESTATE, "pa_seq_swap_in: sequence %lld is not swapped out", (long long)seq);
+  const int32_t nb = (int32_t)s.table.size();
+  if (nb > cap || (nb > 0 && !pairs))
+    return fail(PA_EINVAL, "pa_seq_swap_in: %d pairs do not fit in %d", nb, cap);
+  if (nb > (int32_t)pool->free_stack.size())
+    return fail(PA_ENOMEM, "pa_seq_swap_in: %d blocks needed, %zu free", nb, pool->free_stack.size());
+  for (int32_t i = 0; i < nb; ++i) {
+    const int32_t h = s.table[i];
+    const int32_t b = pool->take();
+    pairs[2 * i] = h;
+    pairs[2 * i + 1] = b;
+    s.table[i] = b;
+    pool->host_free.push_back(h);
+  }
+  s.swapped = false;
+  pool->swapped_seqs -= 1;
+  *num_pairs = nb;
   return PA_OK;
 }
 

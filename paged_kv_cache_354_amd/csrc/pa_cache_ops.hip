@@ -5,8 +5,13 @@
 // blocks are duplicated (copy-on-write) when a sharer writes.  "At a glance":
 // a block is copied only when a sequence writes to it.
 //
-// Both kernels move bytes only (16 bytes per lane, coalesced) and are
-// bitwise exact.  Pool layout: [num_blocks][num_kv_heads][block_size][head_dim].
+// Same page, "How it works" and "Trade-offs": a preempted sequence's blocks
+// can be swapped out to CPU memory and back; pa_swap_blocks copies whole
+// blocks between a device pool and a pool in pinned host memory, which the
+// kernel reads or writes directly over the bus.
+//
+// The kernels move bytes only (16 bytes per lane, coalesced) and are bitwise
+// exact.  Pool layout: [num_blocks][num_kv_heads][block_size][head_dim].
 
 #include <hip/hip_runtime.h>
 
@@ -41,19 +46,21 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
 }
 
 // Workgroup w copies part (w % parts) of pair (w / parts); a block's bytes
-// are split over `parts` workgroups of kThreads lanes.
+// are split over `parts` workgroups of kThreads lanes.  Block src of the
+// source pools goes to block dst of the destination pools (the same pools
+// for copy-on-write); pairs naming a block outside its pool are skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, const int64_t *__restrict__ pairs,
-    int64_t chunks_per_block, int32_t parts, int32_t num_blocks) {
+    const uint4 *src_k, const uint4 *src_v, uint4 *dst_k, uint4 *dst_v, const int64_t *__restrict__ pairs,
+    int64_t chunks_per_block, int32_t parts, int32_t src_blocks, int32_t dst_blocks) {
   int64_t pair = blockIdx.x / parts;
   int32_t part = (int32_t)(blockIdx.x - pair * parts);
   int64_t src = pairs[2 * pair];
   int64_t dst = pairs[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const uint4 *ks = k_cache + src * chunks_per_block;
-  const uint4 *vs = v_cache + src * chunks_per_block;
-  uint4 *kd = k_cache + dst * chunks_per_block;
-  uint4 *vd = v_cache + dst * chunks_per_block;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4 *ks = src_k + src * chunks_per_block;
+  const uint4 *vs = src_v + src * chunks_per_block;
+  uint4 *kd = dst_k + dst * chunks_per_block;
+  uint4 *vd = dst_v + dst * chunks_per_block;
   for (int64_t i = (int64_t)part * kThreads + threadIdx.x; i < chunks_per_block;
        i += (int64_t)parts * kThreads) {
     uint4 a = ks[i];
@@ -62,6 +69,10 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     vd[i] = b;
   }
 }
+
+hipError_t launch_copy(const void *src_k, const void *src_v, void *dst_k, void *dst_v, const pa_cache_t *geom,
+                       int32_t src_blocks, int32_t dst_blocks, const int64_t *pairs, int32_t num_pairs,
+                       void *stream);
 
 int elt_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : dtype == PA_F32 ? 4 : 0; }
 
@@ -106,16 +117,46 @@ extern "C" pa_status_t pa_copy_blocks(void *k_cache, void *v_cache, const pa_cac
   if (num_pairs < 0) return pa::fail(PA_EINVAL, "pa_copy_blocks: num_pairs=%d < 0", num_pairs);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_dst_pairs) return pa::fail(PA_EINVAL, "pa_copy_blocks: NULL pointer");
-  int64_t block_bytes = (int64_t)cache->num_kv_heads * cache->block_size * cache->head_dim *
-                        elt_bytes(cache->dtype);
-  int64_t chunks = block_bytes / 16;
-  int64_t parts = (chunks + kThreads - 1) / kThreads;
-  if (parts > 64) parts = 64;
-  int64_t grid = parts * num_pairs;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, (uint4 *)k_cache, (uint4 *)v_cache, src_dst_pairs, chunks,
-                     (int32_t)parts, cache->num_blocks);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_copy(k_cache, v_cache, k_cache, v_cache, cache, cache->num_blocks, cache->num_blocks,
+                             src_dst_pairs, num_pairs, stream);
   if (e != hipSuccess) return pa::fail(PA_EHIP, "pa_copy_blocks: launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }
+
+extern "C" pa_status_t pa_swap_blocks(const void *src_k, const void *src_v, const pa_cache_t *src_cache,
+                                      void *dst_k, void *dst_v, const pa_cache_t *dst_cache,
+                                      const int64_t *src_dst_pairs, int32_t num_pairs, void *stream) {
+  if (pa_status_t st = check_cache("pa_swap_blocks", src_cache)) return st;
+  if (pa_status_t st = check_cache("pa_swap_blocks", dst_cache)) return st;
+  if (src_cache->block_size != dst_cache->block_size || src_cache->num_kv_heads != dst_cache->num_kv_heads ||
+      src_cache->head_dim != dst_cache->head_dim || src_cache->dtype != dst_cache->dtype)
+    return pa::fail(PA_EINVAL, "pa_swap_blocks: source and destination blocks differ in shape or dtype");
+  if (num_pairs < 0) return pa::fail(PA_EINVAL, "pa_swap_blocks: num_pairs=%d < 0", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_dst_pairs)
+    return pa::fail(PA_EINVAL, "pa_swap_blocks: NULL pointer");
+  if (((uintptr_t)src_k | (uintptr_t)src_v | (uintptr_t)dst_k | (uintptr_t)dst_v) % 16)
+    return pa::fail(PA_EINVAL, "pa_swap_blocks: pools must be 16-byte aligned");
+  hipError_t e = launch_copy(src_k, src_v, dst_k, dst_v, src_cache, src_cache->num_blocks, dst_cache->num_blocks,
+                             src_dst_pairs, num_pairs, stream);
+  if (e != hipSuccess) return pa::fail(PA_EHIP, "pa_swap_blocks: launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+namespace {
+
+hipError_t launch_copy(const void *src_k, const void *src_v, void *dst_k, void *dst_v, const pa_cache_t *geom,
+                       int32_t src_blocks, int32_t dst_blocks, const int64_t *pairs, int32_t num_pairs,
+                       void *stream) {
+  const int64_t block_bytes = (int64_t)geom->num_kv_heads * geom->block_size * geom->head_dim * elt_bytes(geom->dtype);
+  const int64_t chunks = block_bytes / 16;
+  int64_t parts = (chunks + kThreads - 1) / kThreads;
+  if (parts > 64) parts = 64;
+  const int64_t grid = parts * num_pairs;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const uint4 *)src_k, (const uint4 *)src_v, (uint4 *)dst_k, (uint4 *)dst_v, pairs, chunks,
+                     (int32_t)parts, src_blocks, dst_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace

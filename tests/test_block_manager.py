@@ -57,24 +57,32 @@ def state_lib(p, seqs, nb):
     tables = {s: [int(x) for x in p.table(s)] for s in seqs}
     lens = {s: p.length(s) for s in seqs}
     rc = [p.refcount(b) for b in range(nb)]
-    return tables, lens, rc, [int(x) for x in p.free_order()]
+    swapped = {s for s in seqs if p.is_swapped(s)}
+    return (tables, lens, rc, [int(x) for x in p.free_order()], swapped,
+            [int(x) for x in p.host_free_order()])
 
 
 def state_model(m):
     return ({s: list(t) for s, t in m.tables.items()}, dict(m.lens), list(m.refcount),
-            list(reversed(m.free)))
+            list(reversed(m.free)), set(m.swapped), list(reversed(m.host_free)))
 
 
-ops = st.lists(st.tuples(st.sampled_from(["create", "fork", "append", "cow", "release", "batch"]),
+ops = st.lists(st.tuples(st.sampled_from(["create", "fork", "append", "cow", "release", "batch",
+                                          "swap_out", "swap_in"]),
                          st.integers(0, 6), st.integers(0, 6), st.integers(0, 45)), max_size=80)
 
 
 @settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
-@given(ops=ops, nb=st.integers(1, 30), bs=st.sampled_from([1, 2, 4, 8, 16]), seed=st.integers(0, 50))
-def test_matches_model_under_random_ops(ops, nb, bs, seed):
-    order = np.random.default_rng(seed).permutation(nb)
+@given(ops=ops, nb=st.integers(1, 30), hb=st.integers(0, 20), bs=st.sampled_from([1, 2, 4, 8, 16]),
+       seed=st.integers(0, 50))
+def test_matches_model_under_random_ops(ops, nb, hb, bs, seed):
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(nb)
+    horder = rng.permutation(hb)
     m = BM.BlockManagerModel(nb, bs, order)
     p = pkv.BlockPool(nb, bs, order)
+    m.set_swap_space(hb, horder)
+    p.set_swap_space(hb, horder)
     for op, a, b, n in ops:
         if op == "create":
             call_m, call_p = (lambda: m.create(a, n)), (lambda: p.create(a, n))
@@ -86,6 +94,10 @@ def test_matches_model_under_random_ops(ops, nb, bs, seed):
             call_m, call_p = (lambda: m.cow(a, n % 5)), (lambda: p.cow(a, n % 5))
         elif op == "release":
             call_m, call_p = (lambda: m.release(a)), (lambda: p.release(a))
+        elif op == "swap_out":
+            call_m, call_p = (lambda: m.swap_out(a)), (lambda: [tuple(x) for x in p.swap_out(a).tolist()])
+        elif op == "swap_in":
+            call_m, call_p = (lambda: m.swap_in(a)), (lambda: [tuple(x) for x in p.swap_in(a).tolist()])
         else:
             seqs = [a, b, a] if n % 3 == 0 else [a, b]
             call_m = lambda: [(slot, pair) for slot, pair in m.append_batch(seqs)]
@@ -114,6 +126,8 @@ def test_matches_model_under_random_ops(ops, nb, bs, seed):
                 assert rp[1] == [pr for _, pr in rm if pr is not None]
             elif op in ("append", "cow"):
                 assert (tuple(rp) if op == "cow" and rp else rp) == rm
+            elif op in ("swap_out", "swap_in"):
+                assert rp == rm
         assert state_lib(p, list(m.tables), nb) == state_model(m)
     p.close()
 
@@ -151,3 +165,33 @@ def test_bad_arguments():
         p.create(1, 1)
     with pytest.raises(pkv.PoolStateError):
         p.cow(1, 3)
+
+
+def test_swap_hand_worked():
+    """Worked by hand from the swap rules (logical order, LIFO stacks):
+    pool 6 blocks (free order 0..5), swap space 4 host blocks (0..3), bs 2."""
+    for mk in (lambda: BM.BlockManagerModel(6, 2), lambda: pkv.BlockPool(6, 2)):
+        p = mk()
+        p.set_swap_space(4)
+        p.create(1, 5)                      # A: blocks 0, 1, 2
+        p.fork(1, 2)                        # B shares 0, 1, 2 (counts 2)
+        pairs = [tuple(int(v) for v in x) for x in p.swap_out(2)]
+        assert pairs == [(0, 0), (1, 1), (2, 2)]        # host blocks 0, 1, 2 in order
+        rc = p.refcount if isinstance(p, BM.BlockManagerModel) else [p.refcount(b) for b in range(6)]
+        assert list(rc[:3]) == [1, 1, 1]    # shared: A keeps them
+        assert p.is_swapped(2) and not p.is_swapped(1)
+        exhausted = BM.PoolExhausted if isinstance(p, BM.BlockManagerModel) else pkv.PoolExhausted
+        with pytest.raises(exhausted):      # A needs 3 host blocks, 1 is free
+            p.swap_out(1)
+        state = BM.StateError if isinstance(p, BM.BlockManagerModel) else pkv.PoolStateError
+        with pytest.raises(state):          # swapped out: no appends
+            p.append(2)
+        p.release(1)                        # A gone: device blocks 0, 1, 2 free (pushed 0, 1, 2)
+        pairs = [tuple(int(v) for v in x) for x in p.swap_in(2)]
+        assert pairs == [(0, 2), (1, 1), (2, 0)]        # device stack top is 2, then 1, then 0
+        assert [int(x) for x in p.table(2)] == [2, 1, 0]
+        if isinstance(p, BM.BlockManagerModel):
+            assert list(reversed(p.host_free)) == [2, 1, 0, 3]
+        else:
+            assert [int(x) for x in p.host_free_order()] == [2, 1, 0, 3]
+            p.close()
