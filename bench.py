@@ -80,6 +80,12 @@ PREFILL_WORKLOADS = {
     "prefill_chunked": lambda: W.c6_chunked_prefill(),
 }
 PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (causal QK and PV flops)"
+# Swap: a quarter of the Llama-3-8B-shaped batch's sequences swapped out to a
+# pinned host pool and back in (host manager decisions + pa_swap_blocks);
+# GB/s over the host link in each direction.
+SWAP_WORKLOADS = {"swap_llama3_8b": lambda: W.c2_llama8b_b64()}
+SWAP_METRIC = "KV block swap between HBM and pinned host memory: achieved GB/s per direction"
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", f)
@@ -95,7 +101,8 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                   choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(SWAP_WORKLOADS))
     p.add_argument("--partition", type=int, default=None,
                    help="decode partition_size (default: the workload's configuration)")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache decode calls (0: skip)")
@@ -348,6 +355,78 @@ def prefill_main(args, torch, pkv, dev):
     return 0
 
 
+def swap_main(args, torch, pkv, dev):
+    """Each step swaps every fourth sequence out (device -> pinned host) and
+    back in; the host manager picks the blocks, pa_swap_blocks moves them."""
+    log(f"workload {args.workload}: drawing inputs")
+    c = SWAP_WORKLOADS[args.workload]()
+    pool = pkv.BlockPool(c.num_blocks, c.block_size, np.random.default_rng(0).permutation(c.num_blocks))
+    swap_seqs = list(range(0, c.num_seqs, 4))
+    host_blocks = sum(W.ceil_div(int(c.context_lens[s]), c.block_size) for s in swap_seqs)
+    pool.set_swap_space(host_blocks)
+    for s in range(c.num_seqs):
+        pool.create(s, int(c.context_lens[s]))
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kd, vd = dev_t(c.k_cache), dev_t(c.v_cache)
+    shape = (host_blocks,) + tuple(kd.shape[1:])
+    kh = torch.zeros(shape, dtype=torch.bfloat16).pin_memory()
+    vh = torch.zeros(shape, dtype=torch.bfloat16).pin_memory()
+    block_bytes = c.num_kv_heads * c.block_size * c.head_dim * 2 * 2  # K and V
+
+    def plan():
+        """(out pairs, in pairs) of one round trip, from the manager."""
+        outs = np.concatenate([pool.swap_out(s) for s in swap_seqs])
+        ins = np.concatenate([pool.swap_in(s) for s in swap_seqs])
+        return torch.from_numpy(outs).to(dev), torch.from_numpy(ins).to(dev)
+
+    rounds = [plan() for _ in range(max(args.steps, args.warmup, 1))]
+    n_blocks = int(rounds[0][0].shape[0])
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        pkv.pa_swap_blocks(kd, vd, kh, vh, rounds[i][0])
+        pkv.pa_swap_blocks(kh, vh, kd, vd, rounds[i][1])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        pkv.pa_swap_blocks(kd, vd, kh, vh, rounds[i][0])
+        ev[i][1].record()
+        pkv.pa_swap_blocks(kh, vh, kd, vd, rounds[i][1])
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_out = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / 1e3
+    t_in = float(np.mean([b.elapsed_time(e) for _, b, e in ev])) / 1e3
+    moved = n_blocks * block_bytes
+    result = {
+        "metric": SWAP_METRIC,
+        "value": round(2 * moved * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V pools, shuffled block placement)",
+        "config": {"workload": args.workload, "num_seqs_swapped": len(swap_seqs), "blocks_per_direction": n_blocks,
+                   "bytes_per_direction": moved, "block_bytes_k_plus_v": block_bytes},
+        "out_GBps": round(moved / t_out / 1e9, 2),
+        "in_GBps": round(moved / t_in / 1e9, 2),
+        "roofline": {"bound": "pcie", "achieved": round(moved / ((t_out + t_in) / 2) / 1e9, 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(moved / ((t_out + t_in) / 2) / 1e9 / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "copy_blocks_kernel", "avg_launch_us": round((t_out + t_in) / 2 * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    pool.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # --- main ------------------------------------------------------------------------------
 
 def main(argv=None):
@@ -372,6 +451,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     if args.workload in PREFILL_WORKLOADS:
         return prefill_main(args, torch, pkv, dev)
+    if args.workload in SWAP_WORKLOADS:
+        return swap_main(args, torch, pkv, dev)
     make, default_part = WORKLOADS[args.workload]
     partition = default_part if args.partition is None else args.partition
 
