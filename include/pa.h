@@ -355,6 +355,36 @@ pa_status_t pa_seq_swap_out(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t 
  * space.  PA_ENOMEM when the free pool is too small. */
 pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs);
 
+/* Prefix caching (aimodelwiki "PagedAttention", memory sharing: requests
+ * with a common prefix reuse its KV blocks, kept alive by reference counts).
+ * Once enabled, a sequence created from its prompt tokens
+ * (pa_seq_create_cached) registers each of its full blocks under the exact
+ * key (prefix before the block, the block's tokens) -- no hash, so no
+ * collision -- and a later prompt shares the longest run of its leading full
+ * blocks found that way.  A cached block whose count drops to 0 is not freed:
+ * it waits, unreferenced, at the tail of an LRU list, and is found again by
+ * later prompts.  Blocks are taken from the free stack first, then by
+ * evicting the LRU head (its key is forgotten).  A cached block is
+ * immutable: pa_seq_cow copies it even when its count is 1.  Blocks filled
+ * by pa_seq_append are never registered.  Every call succeeds or changes
+ * nothing. */
+pa_status_t pa_pool_enable_prefix_cache(pa_pool *pool);
+/* Cached blocks with count 0 (the LRU list), or -1 for a NULL pool. */
+int32_t pa_pool_num_cached(const pa_pool *pool);
+/* 1 if block is registered in the prefix cache, 0 if not, -1 outside the pool. */
+int32_t pa_pool_is_cached(const pa_pool *pool, int32_t block);
+/* LRU list, least recently released first, into host out[cap]; *n = count. */
+pa_status_t pa_pool_lru_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n);
+/* New sequence holding tokens[0..num_tokens) (host int32): the leading full
+ * blocks found in the cache are shared (counts + 1), the rest are taken
+ * fresh, and the new full blocks are registered.  *num_cached_tokens
+ * receives the number of leading tokens whose KV is already in the pool (a
+ * multiple of block_size); the caller computes and writes only the rest.
+ * PA_ESTATE if caching is off or seq exists, PA_ENOMEM if the fresh blocks
+ * do not fit (free + evictable blocks, not counting the hits themselves). */
+pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *tokens, int32_t num_tokens,
+                                 int32_t *num_cached_tokens);
+
 #ifdef __cplusplus
 }
 #endif

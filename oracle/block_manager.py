@@ -39,9 +39,21 @@ the device block (which returns to the free pool only if no other sequence
 shares it); swapping in takes a device block per host block, in logical
 order, and returns the host blocks; a swapped-out sequence can only be
 swapped in, inspected or released.
+
+Prefix caching (aimodelwiki "PagedAttention": requests sharing a prefix reuse
+its KV blocks across requests, kept alive by reference counts).  Readings:
+when enabled, a sequence created from its prompt tokens registers each of
+its full blocks under the exact key (prefix node of the previous block, the
+block's tokens); node ids are never reused.  A new prompt shares the longest
+run of its full blocks found that way.  A cached block whose count falls to
+0 is kept at the tail of an LRU list instead of the free stack; a block is
+taken from the free stack first, else by evicting the LRU head (its cache
+entry goes).  A cached block is immutable: forcing a private copy of it
+copies even when its count is 1.
 """
 
 import copy
+from collections import OrderedDict
 
 
 class PoolExhausted(Exception):
@@ -67,19 +79,34 @@ class BlockManagerModel:
         self.lens = {}
         self.host_free = []   # host swap blocks, top of stack = end of list
         self.swapped = set()  # sequences whose table names host blocks
+        self.prefix_cache = False
+        self.cache = {}          # (parent node, tokens tuple) -> (block, node)
+        self.block_key = {}      # cached block -> its key
+        self.lru = OrderedDict()  # cached blocks with count 0, least recent first
+        self.next_node = 1
 
     # -- helpers ---------------------------------------------------------
+    def _available(self):
+        return len(self.free) + len(self.lru)
+
     def _take(self):
-        if not self.free:
+        if self.free:
+            blk = self.free.pop()
+        elif self.lru:
+            blk, _ = self.lru.popitem(last=False)  # evict the least recently released
+            del self.cache[self.block_key.pop(blk)]
+        else:
             raise PoolExhausted()
-        blk = self.free.pop()
         self.refcount[blk] = 1
         return blk
 
     def _release(self, blk):
         self.refcount[blk] -= 1
         if self.refcount[blk] == 0:
-            self.free.append(blk)
+            if blk in self.block_key:
+                self.lru[blk] = None
+            else:
+                self.free.append(blk)
 
     def _need(self, seq):
         if seq not in self.tables:
@@ -89,11 +116,13 @@ class BlockManagerModel:
 
     def _atomic(self, fn):
         saved = (list(self.free), list(self.refcount), copy.deepcopy(self.tables), dict(self.lens),
-                 list(self.host_free), set(self.swapped))
+                 list(self.host_free), set(self.swapped), dict(self.cache), dict(self.block_key),
+                 OrderedDict(self.lru), self.next_node)
         try:
             return fn()
         except Exception:
-            self.free, self.refcount, self.tables, self.lens, self.host_free, self.swapped = saved
+            (self.free, self.refcount, self.tables, self.lens, self.host_free, self.swapped, self.cache,
+             self.block_key, self.lru, self.next_node) = saved
             raise
 
     # -- operations -------------------------------------------------------
@@ -165,7 +194,7 @@ class BlockManagerModel:
         if not 0 <= logical_block < len(table):
             raise StateError("logical block out of range")
         src = table[logical_block]
-        if self.refcount[src] == 1:
+        if self.refcount[src] == 1 and src not in self.block_key:
             return None
 
         def run():
@@ -188,6 +217,57 @@ class BlockManagerModel:
         for blk in self.tables.pop(seq):
             self._release(blk)
         del self.lens[seq]
+
+    # -- prefix cache ---------------------------------------------------------
+    def enable_prefix_cache(self):
+        self.prefix_cache = True
+
+    def create_cached(self, seq, tokens):
+        """New sequence holding ``tokens``; shares the longest cached run of
+        its full blocks.  Returns the number of tokens found cached."""
+        if not self.prefix_cache:
+            raise StateError("prefix caching is not enabled")
+        if seq in self.tables:
+            raise StateError(f"sequence {seq} exists")
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        need = -(-len(tokens) // bs)
+        full = len(tokens) // bs
+        hits, parent = [], 0
+        for i in range(full):
+            hit = self.cache.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if hit is None:
+                break
+            hits.append(hit[0])
+            parent = hit[1]
+        idle = sum(1 for b in hits if self.refcount[b] == 0)
+        if need - len(hits) + idle > self._available():
+            raise PoolExhausted()
+        table = []
+        for b in hits:
+            if self.refcount[b] == 0:
+                del self.lru[b]
+            self.refcount[b] += 1
+            table.append(b)
+        for i in range(len(hits), need):
+            b = self._take()
+            table.append(b)
+            if i < full:
+                key = (parent, tuple(tokens[i * bs:(i + 1) * bs]))
+                node = self.next_node
+                self.next_node += 1
+                self.cache[key] = (b, node)
+                self.block_key[b] = key
+                parent = node
+        self.tables[seq] = table
+        self.lens[seq] = len(tokens)
+        return len(hits) * bs
+
+    def is_cached(self, blk):
+        return blk in self.block_key
+
+    def lru_order(self):
+        return list(self.lru)
 
     # -- swap ---------------------------------------------------------------
     def set_swap_space(self, num_host_blocks, host_free_order=None):
@@ -222,7 +302,7 @@ class BlockManagerModel:
         if seq not in self.swapped:
             raise StateError(f"sequence {seq} is not swapped out")
         table = self.tables[seq]
-        if len(table) > len(self.free):
+        if len(table) > self._available():
             raise PoolExhausted()
         pairs = []
         for lb, h in enumerate(table):

@@ -98,6 +98,11 @@ _SIGS = {
     "pa_seq_is_swapped": (_i32, [_vp, _i64]),
     "pa_seq_swap_out": (_i32, [_vp, _i64, _P64, _i32, _P32]),
     "pa_seq_swap_in": (_i32, [_vp, _i64, _P64, _i32, _P32]),
+    "pa_pool_enable_prefix_cache": (_i32, [_vp]),
+    "pa_pool_num_cached": (_i32, [_vp]),
+    "pa_pool_is_cached": (_i32, [_vp, _i32]),
+    "pa_pool_lru_list": (_i32, [_vp, _P32, _i32, _P32]),
+    "pa_seq_create_cached": (_i32, [_vp, _i64, _P32, _i32, _P32]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -446,6 +451,39 @@ def pa_seq_swap_in(pool, seq):
     return _swap("pa_seq_swap_in", pool, seq)
 
 
+def pa_pool_enable_prefix_cache(pool):
+    _check(load().pa_pool_enable_prefix_cache(pool))
+
+
+def pa_pool_num_cached(pool):
+    return int(load().pa_pool_num_cached(pool))
+
+
+def pa_pool_is_cached(pool, block):
+    r = int(load().pa_pool_is_cached(pool, block))
+    if r < 0:
+        raise PagedKVError(PA_EINVAL, f"block {block} outside the pool")
+    return bool(r)
+
+
+def pa_pool_lru_list(pool):
+    n = pa_pool_num_cached(pool)
+    out = np.empty(max(n, 1), dtype=np.int32)
+    got = ctypes.c_int32()
+    _check(load().pa_pool_lru_list(pool, _np_ptr(out, ctypes.c_int32), n, ctypes.byref(got)))
+    return out[:got.value]
+
+
+def pa_seq_create_cached(pool, seq, tokens):
+    """Create ``seq`` from its prompt ``tokens``; returns how many leading
+    tokens were found in the prefix cache."""
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    got = ctypes.c_int32()
+    ptr = _np_ptr(t, ctypes.c_int32) if t.size else None
+    _check(load().pa_seq_create_cached(pool, seq, ptr, int(t.size), ctypes.byref(got)))
+    return got.value
+
+
 def pa_seq_create(pool, seq, num_tokens):
     _check(load().pa_seq_create(pool, seq, num_tokens))
 
@@ -599,6 +637,21 @@ class BlockPool:
 
     def host_free_order(self):
         return pa_pool_host_free_list(self.handle)
+
+    def enable_prefix_cache(self):
+        pa_pool_enable_prefix_cache(self.handle)
+
+    def create_cached(self, seq, tokens):
+        return pa_seq_create_cached(self.handle, seq, tokens)
+
+    def num_cached(self):
+        return pa_pool_num_cached(self.handle)
+
+    def is_cached(self, block):
+        return pa_pool_is_cached(self.handle, block)
+
+    def lru_order(self):
+        return pa_pool_lru_list(self.handle)
 
 
 # --- prepared calls ----------------------------------------------------------------

@@ -28,11 +28,24 @@
 // shares it; swapping in takes a device block per host block and returns the
 // host blocks.  A swapped-out sequence can only be swapped in, inspected or
 // freed.
+//
+// Prefix caching (aimodelwiki "PagedAttention": requests that share a prefix
+// reuse its KV blocks across requests; reference counts keep them alive):
+// when enabled, the full blocks of a sequence created from its prompt tokens
+// are registered under the key (prefix node of the block before it, the
+// block's tokens), an exact key with no hash to collide; node ids are never
+// reused.  A later prompt walks its full blocks through the cache and shares
+// the longest cached run.  A cached block whose count drops to 0 is kept,
+// unreferenced, at the tail of an LRU list; blocks are taken from the free
+// stack first and then by evicting the LRU head (which leaves the cache).
 
 #include <cstdint>
 #include <cstring>
+#include <list>
+#include <map>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pa.h"
@@ -58,14 +71,41 @@ struct pa_pool {
   std::vector<int32_t> host_free;  // host swap blocks; back() is handed out next
   int32_t swapped_seqs = 0;
 
+  // Prefix cache: key (parent node, tokens of the block) -> (block, node).
+  using CacheKey = std::pair<int64_t, std::vector<int32_t>>;
+  bool prefix_cache = false;
+  int64_t next_node = 1;  // node 0 is the empty prefix
+  std::map<CacheKey, std::pair<int32_t, int64_t>> cache;
+  std::vector<const CacheKey *> block_key;  // key of a cached block, or nullptr
+  std::list<int32_t> lru;                   // cached blocks with count 0, least recent first
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+
+  // Blocks a request can still get: free ones and evictable cached ones.
+  size_t available() const { return free_stack.size() + lru.size(); }
+
   int32_t take() {
-    int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {  // evict the least recently released cached block
+      b = lru.front();
+      lru.pop_front();
+      cache.erase(*block_key[b]);
+      block_key[b] = nullptr;
+    }
     refcount[b] = 1;
     return b;
   }
   void release(int32_t b) {
-    if (--refcount[b] == 0) free_stack.push_back(b);
+    if (--refcount[b] == 0) {
+      if (block_key[b]) lru_pos[b] = lru.insert(lru.end(), b);
+      else free_stack.push_back(b);
+    }
+  }
+  // A cached block gains a reference (leaving the LRU list if it had none).
+  void reuse(int32_t b) {
+    if (refcount[b]++ == 0) lru.erase(lru_pos[b]);
   }
   // Blocks one append to `s` needs: 1 for a fresh or copied block, else 0.
   int32_t append_need(const Seq &s) const {
@@ -119,6 +159,8 @@ pa_status_t pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->refcount.assign(num_blocks, 0);
+  p->block_key.assign(num_blocks, nullptr);
+  p->lru_pos.resize(num_blocks);
   p->free_stack.resize(num_blocks);
   std::vector<char> seen(num_blocks, 0);
   for (int32_t i = 0; i < num_blocks; ++i) {
@@ -161,9 +203,9 @@ pa_status_t pa_seq_create(pa_pool *pool, int64_t seq, int32_t num_tokens) {
   if (num_tokens < 0) return fail(PA_EINVAL, "pa_seq_create: num_tokens=%d < 0", num_tokens);
   if (pool->seqs.count(seq)) return fail(PA_ESTATE, "pa_seq_create: sequence %lld exists", (long long)seq);
   int64_t need = ((int64_t)num_tokens + pool->block_size - 1) / pool->block_size;
-  if (need > (int64_t)pool->free_stack.size())
+  if (need > (int64_t)pool->available())
     return fail(PA_ENOMEM, "pa_seq_create: %lld blocks needed, %zu free", (long long)need,
-                pool->free_stack.size());
+                pool->available());
   Seq s;
   s.table.reserve(need);
   for (int64_t i = 0; i < need; ++i) s.table.push_back(pool->take());
@@ -187,7 +229,7 @@ pa_status_t pa_seq_append(pa_pool *pool, int64_t seq, int64_t *slot, int64_t cow
   if (!pool || !slot || !cow_pair) return fail(PA_EINVAL, "pa_seq_append: NULL argument");
   Seq *sq;
   if (pa_status_t st = resident(pool, seq, "pa_seq_append", &sq)) return st;
-  if (pool->append_need(*sq) > (int32_t)pool->free_stack.size())
+  if (pool->append_need(*sq) > (int32_t)pool->available())
     return fail(PA_ENOMEM, "pa_seq_append: free pool is empty");
   pool->append(*sq, slot, cow_pair);
   return PA_OK;
@@ -225,9 +267,9 @@ pa_status_t pa_seq_append_batch(pa_pool *pool, const int64_t *seqs, int32_t n, i
       }
       extra_len[seqs[i]] += 1;
     }
-    if (need > (int64_t)pool->free_stack.size())
+    if (need > (int64_t)pool->available())
       return fail(PA_ENOMEM, "pa_seq_append_batch: %lld blocks needed, %zu free", (long long)need,
-                  pool->free_stack.size());
+                  pool->available());
   }
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -253,8 +295,10 @@ pa_status_t pa_seq_cow(pa_pool *pool, int64_t seq, int32_t logical_block, int64_
     return fail(PA_ESTATE, "pa_seq_cow: logical block %d outside [0, %zu)", logical_block,
                 s.table.size());
   int32_t src = s.table[logical_block];
-  if (pool->refcount[src] == 1) return PA_OK;
-  if (pool->free_stack.empty()) return fail(PA_ENOMEM, "pa_seq_cow: free pool is empty");
+  // private and not in the prefix cache: written in place, no copy (a
+  // cached block is immutable: others may find it by its tokens)
+  if (pool->refcount[src] == 1 && !pool->block_key[src]) return PA_OK;
+  if (pool->available() == 0) return fail(PA_ENOMEM, "pa_seq_cow: free pool is empty");
   int32_t dst = pool->take();
   pool->release(src);
   s.table[logical_block] = dst;
@@ -404,8 +448,8 @@ pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t c
   const int32_t nb = (int32_t)s.table.size();
   if (nb > cap || (nb > 0 && !pairs))
     return fail(PA_EINVAL, "pa_seq_swap_in: %d pairs do not fit in %d", nb, cap);
-  if (nb > (int32_t)pool->free_stack.size())
-    return fail(PA_ENOMEM, "pa_seq_swap_in: %d blocks needed, %zu free", nb, pool->free_stack.size());
+  if (nb > (int32_t)pool->available())
+    return fail(PA_ENOMEM, "pa_seq_swap_in: %d blocks needed, %zu free", nb, pool->available());
   for (int32_t i = 0; i < nb; ++i) {
     const int32_t h = s.table[i];
     const int32_t b = pool->take();
@@ -417,6 +461,79 @@ pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t c
   s.swapped = false;
   pool->swapped_seqs -= 1;
   *num_pairs = nb;
+  return PA_OK;
+}
+
+pa_status_t pa_pool_enable_prefix_cache(pa_pool *pool) {
+  if (!pool) return fail(PA_EINVAL, "pa_pool_enable_prefix_cache: pool is NULL");
+  pool->prefix_cache = true;
+  return PA_OK;
+}
+
+int32_t pa_pool_num_cached(const pa_pool *pool) { return pool ? (int32_t)pool->lru.size() : -1; }
+
+int32_t pa_pool_is_cached(const pa_pool *pool, int32_t block) {
+  if (!pool || block < 0 || block >= pool->num_blocks) return -1;
+  return pool->block_key[block] ? 1 : 0;
+}
+
+pa_status_t pa_pool_lru_list(const pa_pool *pool, int32_t *out, int32_t cap, int32_t *n) {
+  if (!pool || !n) return fail(PA_EINVAL, "pa_pool_lru_list: NULL argument");
+  int32_t total = (int32_t)pool->lru.size();
+  *n = total;
+  if (total > cap || (total > 0 && !out))
+    return fail(PA_EINVAL, "pa_pool_lru_list: %d cached blocks do not fit in %d", total, cap);
+  int32_t i = 0;
+  for (int32_t b : pool->lru) out[i++] = b;
+  return PA_OK;
+}
+
+pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *tokens, int32_t num_tokens,
+                                 int32_t *num_cached_tokens) {
+  if (!pool || !num_cached_tokens || num_tokens < 0 || (num_tokens > 0 && !tokens))
+    return fail(PA_EINVAL, "pa_seq_create_cached: bad argument");
+  *num_cached_tokens = 0;
+  if (!pool->prefix_cache) return fail(PA_ESTATE, "pa_seq_create_cached: prefix caching is not enabled");
+  if (pool->seqs.count(seq)) return fail(PA_ESTATE, "pa_seq_create_cached: sequence %lld exists", (long long)seq);
+  const int32_t bs = pool->block_size;
+  const int32_t need = (int32_t)(((int64_t)num_tokens + bs - 1) / bs);
+  const int32_t full = num_tokens / bs;
+  // Longest cached run of full blocks.
+  std::vector<int32_t> hits;
+  int64_t parent = 0;
+  int32_t idle_hits = 0;  // hits now in the LRU list: they stop being available
+  for (int32_t i = 0; i < full; ++i) {
+    auto it = pool->cache.find({parent, std::vector<int32_t>(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs)});
+    if (it == pool->cache.end()) break;
+    hits.push_back(it->second.first);
+    idle_hits += pool->refcount[it->second.first] == 0;
+    parent = it->second.second;
+  }
+  const int32_t fresh = need - (int32_t)hits.size();
+  if ((size_t)fresh + idle_hits > pool->available())
+    return fail(PA_ENOMEM, "pa_seq_create_cached: %d blocks needed, %zu free", fresh,
+                pool->available() - idle_hits);
+  Seq s;
+  s.table.reserve(need);
+  for (int32_t b : hits) {
+    pool->reuse(b);
+    s.table.push_back(b);
+  }
+  for (int32_t i = (int32_t)hits.size(); i < need; ++i) {
+    const int32_t b = pool->take();
+    s.table.push_back(b);
+    if (i < full) {  // a full block of the prompt: register it
+      const int64_t node = pool->next_node++;
+      auto ins = pool->cache.emplace(
+          pa_pool::CacheKey{parent, std::vector<int32_t>(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs)},
+          std::make_pair(b, node));
+      pool->block_key[b] = &ins.first->first;
+      parent = node;
+    }
+  }
+  s.len = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  *num_cached_tokens = (int32_t)hits.size() * bs;
   return PA_OK;
 }
 

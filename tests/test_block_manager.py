@@ -58,24 +58,84 @@ def state_lib(p, seqs, nb):
     lens = {s: p.length(s) for s in seqs}
     rc = [p.refcount(b) for b in range(nb)]
     swapped = {s for s in seqs if p.is_swapped(s)}
+    cached = [b for b in range(nb) if p.is_cached(b)]
     return (tables, lens, rc, [int(x) for x in p.free_order()], swapped,
-            [int(x) for x in p.host_free_order()])
+            [int(x) for x in p.host_free_order()], cached, [int(x) for x in p.lru_order()])
 
 
 def state_model(m):
     return ({s: list(t) for s, t in m.tables.items()}, dict(m.lens), list(m.refcount),
-            list(reversed(m.free)), set(m.swapped), list(reversed(m.host_free)))
+            list(reversed(m.free)), set(m.swapped), list(reversed(m.host_free)),
+            [b for b in range(m.num_blocks) if m.is_cached(b)], m.lru_order())
+
+
+def prompt(b, n):
+    """Prompt of n tokens from family b: families share a repeating prefix
+    up to a family-dependent split, then diverge (so cache hits, partial hits
+    and misses all occur)."""
+    split = (b * 7) % (n + 1)
+    return [i % 5 if i < split else (b + i) % 7 for i in range(n)]
 
 
 ops = st.lists(st.tuples(st.sampled_from(["create", "fork", "append", "cow", "release", "batch",
-                                          "swap_out", "swap_in"]),
+                                          "swap_out", "swap_in", "cached", "cached"]),
                          st.integers(0, 6), st.integers(0, 6), st.integers(0, 45)), max_size=80)
 
 
-@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
-@given(ops=ops, nb=st.integers(1, 30), hb=st.integers(0, 20), bs=st.sampled_from([1, 2, 4, 8, 16]),
-       seed=st.integers(0, 50))
-def test_matches_model_under_random_ops(ops, nb, hb, bs, seed):
+def step(m, p, nb, op, a, b, n):
+    """Apply one operation to the model and the library; both must agree on
+    the result or the error, and on the whole pool state afterwards."""
+    if op == "create":
+        call_m, call_p = (lambda: m.create(a, n)), (lambda: p.create(a, n))
+    elif op == "fork":
+        call_m, call_p = (lambda: m.fork(a, b)), (lambda: p.fork(a, b))
+    elif op == "append":
+        call_m, call_p = (lambda: m.append(a)), (lambda: p.append(a))
+    elif op == "cow":
+        call_m, call_p = (lambda: m.cow(a, n % 5)), (lambda: p.cow(a, n % 5))
+    elif op == "release":
+        call_m, call_p = (lambda: m.release(a)), (lambda: p.release(a))
+    elif op == "swap_out":
+        call_m, call_p = (lambda: m.swap_out(a)), (lambda: [tuple(x) for x in p.swap_out(a).tolist()])
+    elif op == "swap_in":
+        call_m, call_p = (lambda: m.swap_in(a)), (lambda: [tuple(x) for x in p.swap_in(a).tolist()])
+    elif op == "cached":
+        toks = prompt(b, n)
+        call_m, call_p = (lambda: m.create_cached(a, toks)), (lambda: p.create_cached(a, toks))
+    else:
+        seqs = [a, b, a] if n % 3 == 0 else [a, b]
+        call_m = lambda: [(slot, pair) for slot, pair in m.append_batch(seqs)]
+
+        def call_p():
+            slots, pairs = p.append_batch(seqs)
+            return slots.tolist(), [tuple(x) for x in pairs.tolist()]
+    try:
+        rm = call_m()
+        em = None
+    except BM.PoolExhausted:
+        rm, em = None, "enomem"
+    except BM.StateError:
+        rm, em = None, "state"
+    try:
+        rp = call_p()
+        ep = None
+    except pkv.PoolExhausted:
+        rp, ep = None, "enomem"
+    except pkv.PoolStateError:
+        rp, ep = None, "state"
+    assert em == ep, (op, a, b, n)
+    if em is None:
+        if op == "batch":
+            assert rp[0] == [s for s, _ in rm]
+            assert rp[1] == [pr for _, pr in rm if pr is not None]
+        elif op in ("append", "cow"):
+            assert (tuple(rp) if op == "cow" and rp else rp) == rm
+        elif op in ("swap_out", "swap_in", "cached"):
+            assert rp == rm
+    assert state_lib(p, list(m.tables), nb) == state_model(m), (op, a, b, n)
+
+
+def pair_of_pools(nb, bs, hb, seed, cache):
     rng = np.random.default_rng(seed)
     order = rng.permutation(nb)
     horder = rng.permutation(hb)
@@ -83,53 +143,36 @@ def test_matches_model_under_random_ops(ops, nb, hb, bs, seed):
     p = pkv.BlockPool(nb, bs, order)
     m.set_swap_space(hb, horder)
     p.set_swap_space(hb, horder)
-    for op, a, b, n in ops:
-        if op == "create":
-            call_m, call_p = (lambda: m.create(a, n)), (lambda: p.create(a, n))
-        elif op == "fork":
-            call_m, call_p = (lambda: m.fork(a, b)), (lambda: p.fork(a, b))
-        elif op == "append":
-            call_m, call_p = (lambda: m.append(a)), (lambda: p.append(a))
-        elif op == "cow":
-            call_m, call_p = (lambda: m.cow(a, n % 5)), (lambda: p.cow(a, n % 5))
-        elif op == "release":
-            call_m, call_p = (lambda: m.release(a)), (lambda: p.release(a))
-        elif op == "swap_out":
-            call_m, call_p = (lambda: m.swap_out(a)), (lambda: [tuple(x) for x in p.swap_out(a).tolist()])
-        elif op == "swap_in":
-            call_m, call_p = (lambda: m.swap_in(a)), (lambda: [tuple(x) for x in p.swap_in(a).tolist()])
-        else:
-            seqs = [a, b, a] if n % 3 == 0 else [a, b]
-            call_m = lambda: [(slot, pair) for slot, pair in m.append_batch(seqs)]
+    if cache:
+        m.enable_prefix_cache()
+        p.enable_prefix_cache()
+    return m, p
 
-            def call_p():
-                slots, pairs = p.append_batch(seqs)
-                return slots.tolist(), [tuple(x) for x in pairs.tolist()]
-        try:
-            rm = call_m()
-            em = None
-        except BM.PoolExhausted:
-            rm, em = None, "enomem"
-        except BM.StateError:
-            rm, em = None, "state"
-        try:
-            rp = call_p()
-            ep = None
-        except pkv.PoolExhausted:
-            rp, ep = None, "enomem"
-        except pkv.PoolStateError:
-            rp, ep = None, "state"
-        assert em == ep, (op, a, b, n)
-        if em is None:
-            if op == "batch":
-                assert rp[0] == [s for s, _ in rm]
-                assert rp[1] == [pr for _, pr in rm if pr is not None]
-            elif op in ("append", "cow"):
-                assert (tuple(rp) if op == "cow" and rp else rp) == rm
-            elif op in ("swap_out", "swap_in"):
-                assert rp == rm
-        assert state_lib(p, list(m.tables), nb) == state_model(m)
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(ops=ops, nb=st.integers(1, 30), hb=st.integers(0, 20), bs=st.sampled_from([1, 2, 4, 8, 16]),
+       seed=st.integers(0, 50))
+def test_matches_model_under_random_ops(ops, nb, hb, bs, seed):
+    # a quarter of the runs keep prefix caching off (create_cached is then an error)
+    m, p = pair_of_pools(nb, bs, hb, seed, cache=seed % 4 != 0)
+    for op, a, b, n in ops:
+        step(m, p, nb, op, a, b, n)
     p.close()
+
+
+def test_matches_model_long_seeded_runs():
+    """Uniformly drawn operation runs of up to 80 steps: unlike the shrinking
+    search above, these often fill the pool with cached blocks, so eviction
+    from an LRU list of several blocks (and its order) is exercised."""
+    rng = np.random.default_rng(2024)
+    names = ["create", "fork", "append", "cow", "release", "batch", "swap_out", "swap_in", "cached", "cached"]
+    for run in range(300):
+        nb = int(rng.integers(1, 31))
+        m, p = pair_of_pools(nb, int(rng.choice([1, 2, 4, 8, 16])), int(rng.integers(0, 21)), run, cache=True)
+        for _ in range(int(rng.integers(0, 81))):
+            step(m, p, nb, names[int(rng.integers(len(names)))], int(rng.integers(7)), int(rng.integers(7)),
+                 int(rng.integers(46)))
+        p.close()
 
 
 def test_tables_export_pads_with_minus_one():
@@ -194,4 +237,59 @@ def test_swap_hand_worked():
             assert list(reversed(p.host_free)) == [2, 1, 0, 3]
         else:
             assert [int(x) for x in p.host_free_order()] == [2, 1, 0, 3]
+            p.close()
+
+
+def test_prefix_cache_hand_worked():
+    """Worked by hand from the prefix-cache rules (exact keys on full blocks,
+    count-0 cached blocks kept in LRU order, free stack before eviction,
+    cached blocks immutable): pool 6 blocks (free order 0..5), bs 2."""
+    for is_model in (True, False):
+        p = BM.BlockManagerModel(6, 2) if is_model else pkv.BlockPool(6, 2)
+        exhausted = BM.PoolExhausted if is_model else pkv.PoolExhausted
+        state = BM.StateError if is_model else pkv.PoolStateError
+
+        def rc():
+            return list(p.refcount) if is_model else [p.refcount(b) for b in range(6)]
+
+        def free():
+            return list(reversed(p.free)) if is_model else [int(x) for x in p.free_order()]
+
+        def table(s):
+            return [int(x) for x in p.table(s)]
+
+        with pytest.raises(state):                      # caching not enabled yet
+            p.create_cached(1, [1, 2])
+        p.enable_prefix_cache()
+        assert p.create_cached(1, [1, 2, 3, 4, 5]) == 0  # blocks 0, 1 (cached), 2 (partial)
+        assert table(1) == [0, 1, 2]
+        assert p.create_cached(2, [1, 2, 3, 4, 9, 9, 7]) == 4  # shares 0, 1; fresh 3 (cached), 4
+        assert table(2) == [0, 1, 3, 4]
+        assert rc() == [2, 2, 1, 1, 1, 0]
+        assert [b for b in range(6) if p.is_cached(b)] == [0, 1, 3]
+        p.release(1)                                    # 2 is not cached: back to the free stack
+        p.release(2)                                    # 0, 1, 3 wait in the LRU list; 4 is freed
+        assert list(p.lru_order()) == [0, 1, 3]
+        assert free() == [4, 2, 5]
+        assert p.create_cached(3, [1, 2]) == 2           # hit 0 leaves the LRU list
+        assert table(3) == [0] and list(p.lru_order()) == [1, 3]
+        p.create(4, 10)                                 # free stack 4, 2, 5, then evicts 1, then 3
+        assert table(4) == [4, 2, 5, 1, 3]
+        assert not p.is_cached(1) and not p.is_cached(3) and list(p.lru_order()) == []
+        with pytest.raises(exhausted):                  # [3, 4] after [1, 2] was evicted
+            p.create_cached(5, [1, 2, 3, 4])
+        with pytest.raises(exhausted):                  # block 0 is private but cached: must copy
+            p.cow(3, 0)
+        p.release(4)                                    # free stack (top first) 3, 1, 5, 2, 4
+        assert free() == [3, 1, 5, 2, 4]
+        pair = p.cow(3, 0)
+        assert tuple(int(v) for v in pair) == (0, 3)
+        assert table(3) == [3] and list(p.lru_order()) == [0]
+        assert p.create_cached(6, [1, 2, 5, 5]) == 2     # 0 from the LRU list, fresh 1 (cached)
+        assert table(6) == [0, 1] and list(p.lru_order()) == []
+        assert p.create_cached(7, [1, 2, 5, 5, 8]) == 4  # shares 0, 1; fresh 5 for the partial block
+        assert table(7) == [0, 1, 5]
+        assert rc() == [2, 2, 0, 1, 0, 1]
+        assert not p.is_cached(5)
+        if not is_model:
             p.close()
