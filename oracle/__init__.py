@@ -32,7 +32,12 @@ What it computes, and where the pages define it:
 * ``block_manager.BlockManagerModel`` -- free pool, reference counts, on-demand
   table extension, sharing, copy-on-write and release (foundry page,
   *Concept*, *How it works*, *At a glance*; aiacademy lesson "Paged
-  Attention", the virtual-memory analogy table).
+  Attention", the virtual-memory analogy table); also its swap space and
+  prefix cache (foundry page, *How it works* and *Trade-offs*; aimodelwiki
+  "PagedAttention" glossary entry, prefix-caching paragraph).
+* ``waste.simulate`` -- a serving loop over one pool of KV slots, contiguous
+  slabs against paged blocks, counting live and held slots per step (foundry
+  page, *Concept* and *At a glance*; aiacademy lesson, its toy memory map).
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against
 something other than itself: brute-force loops on tiny inputs, PyTorch's
@@ -41,4 +46,4 @@ hand-worked golden fixtures under ``tests/golden/`` and invariants the pages
 state (placement independence, sharing, tail blocks).
 """
 
-from . import attention, block_manager, kvcache, numerics, prefill  # noqa: F401
+from . import attention, block_manager, kvcache, numerics, prefill, waste  # noqa: F401
