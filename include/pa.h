@@ -355,8 +355,10 @@ pa_status_t pa_seq_swap_out(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t 
  * space.  PA_ENOMEM when the free pool is too small. */
 pa_status_t pa_seq_swap_in(pa_pool *pool, int64_t seq, int64_t *pairs, int32_t cap, int32_t *num_pairs);
 
-/* Prefix caching (aimodelwiki "PagedAttention", memory sharing: requests
- * with a common prefix reuse its KV blocks, kept alive by reference counts).
+/* Prefix caching (aimodelwiki "PagedAttention" glossary entry, the paragraph
+ * on prefix caching: prompt prefixes shared across requests reuse KV pages
+ * already computed; foundry "PagedAttention" ops page, At a glance: shared
+ * blocks are tracked by reference count).
  * Once enabled, a sequence created from its prompt tokens
  * (pa_seq_create_cached) registers each of its full blocks under the exact
  * key (prefix before the block, the block's tokens) -- no hash, so no
@@ -384,6 +386,49 @@ pa_status_t pa_pool_lru_list(const pa_pool *pool, int32_t *out, int32_t cap, int
  * do not fit (free + evictable blocks, not counting the hits themselves). */
 pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *tokens, int32_t num_tokens,
                                  int32_t *num_cached_tokens);
+
+/* ------------------------------------------------------------------------
+ * KV-cache waste of a serving loop (host only).
+ *
+ * foundry "PagedAttention" ops page, Concept and At a glance: a contiguous
+ * slab per request, sized to its maximum length, strands its unfilled slots
+ * and leaves gaps too small to reuse; paged blocks, handed out one at a time
+ * on demand, waste at most one partly filled block per sequence.  aiacademy
+ * "Paged Attention" lesson: the slab is sized for the longest output the
+ * request might produce.
+ *
+ * pa_waste_simulate runs num_requests requests (all queued at step 0, in
+ * order) through one pool of capacity KV token slots until all finish.
+ * Request i has a prompt of prompt_lens[i] >= 1 tokens, generates
+ * output_lens[i] >= 1 tokens and, contiguous, reserves a slab of
+ * reserve_lens[i] >= p + o slots (host int32 arrays).  Each step: admit
+ * from the head of the queue while it fits (PA_WASTE_CONTIGUOUS: first fit,
+ * the lowest-addressed free gap of at least r slots, freed slabs merge with
+ * free neighbours; PA_WASTE_PAGED: ceil(p / block_size) blocks of this
+ * library's block manager over capacity / block_size blocks); record the
+ * counters below; store one token for every running request (paged: a
+ * request needing a block when none is free preempts the most recently
+ * admitted running request -- its blocks freed, its progress lost, back to
+ * the front of the queue -- until a block is free or it preempted itself);
+ * retire finished requests.  *out receives the totals.  PA_EINVAL for a
+ * request that cannot fit in the pool alone or breaks p >= 1, o >= 1,
+ * r >= p + o. */
+#define PA_WASTE_CONTIGUOUS 0
+#define PA_WASTE_PAGED 1
+typedef struct pa_waste_stats {
+  int64_t steps;
+  int64_t live_slot_steps;    /* sum over steps of tokens stored by running requests */
+  int64_t held_slot_steps;    /* sum over steps of slots they hold (slabs, or blocks x block_size) */
+  int64_t running_steps;      /* sum over steps of running requests */
+  int64_t max_running;
+  int64_t preemptions;        /* paged only */
+  int64_t frag_blocked_steps; /* contiguous: steps whose queue head was refused although the
+                                 free slots added up to its slab */
+  int64_t decode_tokens;      /* tokens stored after admission, including ones lost to preemption */
+} pa_waste_stats;
+pa_status_t pa_waste_simulate(int32_t mode, int64_t capacity, int32_t block_size, const int32_t *prompt_lens,
+                              const int32_t *output_lens, const int32_t *reserve_lens, int32_t num_requests,
+                              pa_waste_stats *out);
 
 #ifdef __cplusplus
 }

@@ -40,8 +40,9 @@ shares it); swapping in takes a device block per host block, in logical
 order, and returns the host blocks; a swapped-out sequence can only be
 swapped in, inspected or released.
 
-Prefix caching (aimodelwiki "PagedAttention": requests sharing a prefix reuse
-its KV blocks across requests, kept alive by reference counts).  Readings:
+Prefix caching (aimodelwiki "PagedAttention" glossary entry, prefix-caching
+paragraph: requests sharing a prompt prefix reuse its KV blocks; foundry ops
+page, At a glance: shared blocks are tracked by reference count).  Readings:
 when enabled, a sequence created from its prompt tokens registers each of
 its full blocks under the exact key (prefix node of the previous block, the
 block's tokens); node ids are never reused.  A new prompt shares the longest

@@ -29,12 +29,14 @@
 // host blocks.  A swapped-out sequence can only be swapped in, inspected or
 // freed.
 //
-// Prefix caching (aimodelwiki "PagedAttention": requests that share a prefix
-// reuse its KV blocks across requests; reference counts keep them alive):
+// Prefix caching (aimodelwiki "PagedAttention" glossary entry, prefix-caching
+// paragraph: requests that share a prompt prefix reuse its KV blocks; foundry
+// ops page, At a glance: shared blocks are tracked by reference count):
 // when enabled, the full blocks of a sequence created from its prompt tokens
 // are registered under the key (prefix node of the block before it, the
-// block's tokens), an exact key with no hash to collide; node ids are never
-// reused.  A later prompt walks its full blocks through the cache and shares
+// block's tokens); lookups go through a 64-bit hash of that key and then
+// compare the key itself, so a hash collision can never share wrong KV; node
+// ids are never reused.  A later prompt walks its full blocks through the cache and shares
 // the longest cached run.  A cached block whose count drops to 0 is kept,
 // unreferenced, at the tail of an LRU list; blocks are taken from the free
 // stack first and then by evicting the LRU head (which leaves the cache).
@@ -42,7 +44,7 @@
 #include <cstdint>
 #include <cstring>
 #include <list>
-#include <map>
+#include <algorithm>
 #include <new>
 #include <unordered_map>
 #include <utility>
@@ -71,12 +73,51 @@ struct pa_pool {
   std::vector<int32_t> host_free;  // host swap blocks; back() is handed out next
   int32_t swapped_seqs = 0;
 
-  // Prefix cache: key (parent node, tokens of the block) -> (block, node).
-  using CacheKey = std::pair<int64_t, std::vector<int32_t>>;
+  // Prefix cache: key (parent node, tokens of the block) -> (block, node),
+  // found by the key's hash and confirmed by comparing the key.
+  struct CacheEntry {
+    int64_t parent;
+    std::vector<int32_t> tokens;
+    int32_t block;
+    int64_t node;
+  };
   bool prefix_cache = false;
   int64_t next_node = 1;  // node 0 is the empty prefix
-  std::map<CacheKey, std::pair<int32_t, int64_t>> cache;
-  std::vector<const CacheKey *> block_key;  // key of a cached block, or nullptr
+  std::unordered_multimap<uint64_t, CacheEntry> cache;  // elements keep their address on rehash
+  std::vector<const CacheEntry *> block_key;            // entry of a cached block, or nullptr
+  std::vector<uint64_t> block_hash;
+
+  static uint64_t key_hash(int64_t parent, const int32_t *tok, int32_t n) {
+    // FNV-1a over the parent id and the token ids, then a final avalanche
+    uint64_t h = 0xcbf29ce484222325ull ^ (uint64_t)parent;
+    h *= 0x100000001b3ull;
+    for (int32_t i = 0; i < n; ++i) {
+      h ^= (uint32_t)tok[i];
+      h *= 0x100000001b3ull;
+    }
+    h ^= h >> 33;
+    h *= 0xff51afd7ed558ccdull;
+    h ^= h >> 33;
+    return h;
+  }
+  const CacheEntry *find(uint64_t h, int64_t parent, const int32_t *tok, int32_t n) const {
+    auto range = cache.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it) {
+      const CacheEntry &e = it->second;
+      if (e.parent == parent && std::equal(e.tokens.begin(), e.tokens.end(), tok, tok + n)) return &e;
+    }
+    return nullptr;
+  }
+  void forget(int32_t b) {  // drop a cached block's entry
+    auto range = cache.equal_range(block_hash[b]);
+    for (auto it = range.first; it != range.second; ++it) {
+      if (&it->second == block_key[b]) {
+        cache.erase(it);
+        break;
+      }
+    }
+    block_key[b] = nullptr;
+  }
   std::list<int32_t> lru;                   // cached blocks with count 0, least recent first
   std::vector<std::list<int32_t>::iterator> lru_pos;
 
@@ -91,8 +132,7 @@ struct pa_pool {
     } else {  // evict the least recently released cached block
       b = lru.front();
       lru.pop_front();
-      cache.erase(*block_key[b]);
-      block_key[b] = nullptr;
+      forget(b);
     }
     refcount[b] = 1;
     return b;
@@ -160,6 +200,7 @@ pa_status_t pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
   p->block_size = block_size;
   p->refcount.assign(num_blocks, 0);
   p->block_key.assign(num_blocks, nullptr);
+  p->block_hash.assign(num_blocks, 0);
   p->lru_pos.resize(num_blocks);
   p->free_stack.resize(num_blocks);
   std::vector<char> seen(num_blocks, 0);
@@ -503,11 +544,12 @@ pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *toke
   int64_t parent = 0;
   int32_t idle_hits = 0;  // hits now in the LRU list: they stop being available
   for (int32_t i = 0; i < full; ++i) {
-    auto it = pool->cache.find({parent, std::vector<int32_t>(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs)});
-    if (it == pool->cache.end()) break;
-    hits.push_back(it->second.first);
-    idle_hits += pool->refcount[it->second.first] == 0;
-    parent = it->second.second;
+    const int32_t *tok = tokens + (int64_t)i * bs;
+    const pa_pool::CacheEntry *e = pool->find(pa_pool::key_hash(parent, tok, bs), parent, tok, bs);
+    if (!e) break;
+    hits.push_back(e->block);
+    idle_hits += pool->refcount[e->block] == 0;
+    parent = e->node;
   }
   const int32_t fresh = need - (int32_t)hits.size();
   if ((size_t)fresh + idle_hits > pool->available())
@@ -523,11 +565,12 @@ pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *toke
     const int32_t b = pool->take();
     s.table.push_back(b);
     if (i < full) {  // a full block of the prompt: register it
+      const int32_t *tok = tokens + (int64_t)i * bs;
       const int64_t node = pool->next_node++;
-      auto ins = pool->cache.emplace(
-          pa_pool::CacheKey{parent, std::vector<int32_t>(tokens + (int64_t)i * bs, tokens + (int64_t)(i + 1) * bs)},
-          std::make_pair(b, node));
-      pool->block_key[b] = &ins.first->first;
+      const uint64_t h = pa_pool::key_hash(parent, tok, bs);
+      auto it = pool->cache.emplace(h, pa_pool::CacheEntry{parent, std::vector<int32_t>(tok, tok + bs), b, node});
+      pool->block_key[b] = &it->second;
+      pool->block_hash[b] = h;
       parent = node;
     }
   }
