@@ -86,6 +86,19 @@ PREFILL_METRIC = "paged prefill attention: achieved TFLOP/s (causal QK and PV fl
 SWAP_WORKLOADS = {"swap_llama3_8b": lambda: W.c2_llama8b_b64()}
 SWAP_METRIC = "KV block swap between HBM and pinned host memory: achieved GB/s per direction"
 HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction
+# Prefix-cached prompt admission: each step admits 64 Llama-3-8B-shaped
+# requests (a cached 2048-token system prompt + private suffixes); the host
+# manager finds the cached blocks, only the uncached tokens are stored and
+# prefilled.  Prompt tokens admitted per second, beside the same batch
+# admitted without the cache.
+PREFIX_WORKLOADS = {"prefix_cached_prompts": lambda: W.c8_prefix_cached_prompts()}
+PREFIX_METRIC = "prefix-cached prompt admission: prompt tokens/s (cached + computed)"
+# KV waste of a serving loop (host simulation, no kernel): 4096 requests
+# through the KV slots one MI355X holds for Llama-3-8B, contiguous slabs
+# against the library's paged block manager (bs 16).
+WASTE_WORKLOADS = {"waste_llama3_8b_c2": lambda: W.waste_case("waste_llama3_8b_c2"),
+                   "waste_llama3_8b_c5": lambda: W.waste_case("waste_llama3_8b_c5")}
+WASTE_METRIC = "KV-cache waste: % of held KV slots holding no token (paged blocks; contiguous slabs beside)"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", f)
@@ -102,7 +115,8 @@ def parse_args(argv=None):
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                   choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(SWAP_WORKLOADS))
+                   choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(SWAP_WORKLOADS)
+                   + sorted(PREFIX_WORKLOADS) + sorted(WASTE_WORKLOADS))
     p.add_argument("--partition", type=int, default=None,
                    help="decode partition_size (default: the workload's configuration)")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache decode calls (0: skip)")
@@ -233,18 +247,22 @@ def cpu_baseline(case, plan, budget_s):
             "tokens_per_s": round(done_tok / dt, 1), "seconds": round(dt, 2)}
 
 
-def prefill_flops(pc):
+def causal_flops(context_lens, cu_seqlens, num_q_heads, head_dim):
     """Algorithmic flops of one pa_prefill call: for every (query, visible
     key, query head), 2d for q.k and 2d for p.v."""
-    lens = pc.case.context_lens.astype(np.int64)
-    nq = np.diff(pc.cu_seqlens).astype(np.int64)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    nq = np.diff(np.asarray(cu_seqlens, dtype=np.int64))
     pairs = 0
     for ctx, n in zip(lens, nq):
         first = ctx - n  # position of the first query
         # sum over i < n of (first + i + 1) visible keys, clipped at 0
         pos = np.arange(n, dtype=np.int64) + first + 1
         pairs += int(np.clip(pos, 0, None).sum())
-    return pairs * pc.case.num_q_heads * 4 * pc.case.head_dim
+    return pairs * num_q_heads * 4 * head_dim
+
+
+def prefill_flops(pc):
+    return causal_flops(pc.case.context_lens, pc.cu_seqlens, pc.case.num_q_heads, pc.case.head_dim)
 
 
 def prefill_cpu_baseline(pc, budget_s):
@@ -427,6 +445,253 @@ def swap_main(args, torch, pkv, dev):
     return 0
 
 
+def prefix_cpu_baseline(plan, budget_s):
+    """fp64 oracle rows (every head of a token) for suffix queries drawn at
+    random, attending over the request's whole prompt (the cached path's
+    work); prompt tokens/s = computed rows/s x prompt tokens per computed
+    token."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import prefill as P
+
+    bs, hkv, d = plan.block_size, plan.num_kv_heads, plan.head_dim
+    grp = plan.num_q_heads // hkv
+    cu = plan.suffix_cu
+    rng = np.random.default_rng(0)
+    pools = {}
+
+    def pool_of(s):
+        """Request s's whole prompt K/V laid out as a private contiguous pool."""
+        if s not in pools:
+            n = plan.prefix_len + int(plan.suffix_lens[s])
+            nb = W.ceil_div(n, bs)
+            out = []
+            for pre, suf in ((plan.prefix_k, plan.suffix_k), (plan.prefix_v, plan.suffix_v)):
+                rows = np.zeros((nb * bs, hkv, d), np.uint16)
+                rows[:plan.prefix_len] = pre
+                rows[plan.prefix_len:n] = suf[cu[s]:cu[s + 1]]
+                out.append(rows.reshape(nb, bs, hkv, d).transpose(0, 2, 1, 3).copy())
+            pools.clear()
+            pools[s] = (out[0], out[1], np.arange(nb, dtype=np.int32), n)
+        return pools[s]
+
+    rows_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        s = int(rng.integers(plan.num_seqs))
+        kc, vc, table, n = pool_of(s)
+        for i in rng.integers(0, int(plan.suffix_lens[s]), 8):
+            pos = plan.prefix_len + int(i)
+            for h in range(plan.num_q_heads):
+                P.prefill_row(plan.suffix_q[cu[s] + i, h], kc, vc, table, n, pos, plan.scale, plan.dtype, h // grp)
+            rows_done += 1
+    dt = time.perf_counter() - t0
+    prompt_tokens = plan.num_seqs * plan.prefix_len + int(plan.suffix_lens.sum())
+    per_computed = prompt_tokens / int(plan.suffix_lens.sum())
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(rows_done / dt * per_computed, 3), "unit": "prompt tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 oracle rows (all {plan.num_q_heads} heads of a token) for {rows_done} suffix queries "
+                      f"drawn at random, each over its whole prompt, {dt:.1f} s wall; scaled by "
+                      f"{per_computed:.2f} prompt tokens per computed token", "seconds": round(dt, 2)}
+
+
+def prefix_main(args, torch, pkv, dev):
+    """Admission of a batch of prompts sharing a cached system prompt.
+
+    Host (planned before the timed region, timed on its own): for each
+    request the manager's create_cached, the slots of its uncached tokens
+    and the batch tables; the batch is released after the step (the system
+    prompt's blocks go back to the LRU list, where the next step finds
+    them).  Device, per step: pa_write_kv of the uncached tokens, then
+    pa_prefill of their queries over the whole prompts.  The same batch
+    without the cache (every prompt stored and prefilled whole) is timed
+    beside it."""
+    log(f"workload {args.workload}: drawing inputs")
+    plan = PREFIX_WORKLOADS[args.workload]()
+    B, bs = plan.num_seqs, plan.block_size
+    nsteps = args.warmup + args.steps
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    shape = (plan.num_blocks, plan.num_kv_heads, bs, plan.head_dim)
+    kc, vc = torch.zeros(shape, dtype=torch.bfloat16, device=dev), torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    pool = pkv.BlockPool(plan.num_blocks, bs, plan.free_order)
+    pool.enable_prefix_cache()
+    # the system prompt is already cached when the measured traffic starts
+    assert pool.create_cached(-1, plan.prefix_tokens) == 0
+    pkv.pa_write_kv(dev_t(plan.prefix_k), dev_t(plan.prefix_v),
+                    dev_t(np.asarray(pool.slots(-1, 0, plan.prefix_len), np.int64)), kc, vc)
+    pool.release(-1)
+
+    log(f"planning {nsteps} steps with the host manager")
+    lens = (plan.prefix_len + plan.suffix_lens).astype(np.int32)
+    mb = W.ceil_div(int(lens.max()), bs)
+    host_s, plans, cached_tokens = 0.0, [], 0
+    for t in range(nsteps):
+        prompts = [plan.prompt(t, s) for s in range(B)]
+        t0 = time.perf_counter()
+        cached = [pool.create_cached(s, prompts[s]) for s in range(B)]
+        slots = np.concatenate([np.asarray(pool.slots(s, cached[s], int(lens[s]) - cached[s]), np.int64)
+                                for s in range(B)])
+        tables, ctx = pool.tables(list(range(B)), mb)
+        for s in range(B):
+            pool.release(s)
+        host_s += time.perf_counter() - t0
+        if any(c != plan.prefix_len for c in cached):
+            raise RuntimeError(f"step {t}: expected the {plan.prefix_len}-token system prompt cached, got {cached}")
+        cached_tokens += sum(cached)
+        plans.append((dev_t(slots), dev_t(tables)))
+    cu = dev_t(plan.suffix_cu)
+    ctx_d = dev_t(lens)
+    q, kn, vn = dev_t(plan.suffix_q), dev_t(plan.suffix_k), dev_t(plan.suffix_v)
+    out = torch.empty_like(q)
+    max_q = int(plan.suffix_lens.max())
+    steps = [(pkv.prepare_write_kv(kn, vn, slots, kc, vc),
+              pkv.prepare_prefill(q, kc, vc, tables, ctx_d, cu, max_q, int(lens.max()), plan.scale, out))
+             for slots, tables in plans]
+
+    def timed(calls, kernel_index):
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            for c in calls[i % len(calls)]:
+                c()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            for c in calls[(args.warmup + i) % len(calls)]:
+                c()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            calls[(args.warmup + i) % len(calls)][kernel_index]()
+        e1.record()
+        torch.cuda.synchronize()
+        return wall / args.steps, e0.elapsed_time(e1) / 1e3 / args.steps
+
+    log(f"timed {args.steps} cached steps")
+    step_s, prefill_s = timed(steps, 1)
+
+    log("uncached comparison: every prompt stored and prefilled whole")
+    pool_u = pkv.BlockPool(plan.num_blocks, bs, plan.free_order)
+    for s in range(B):
+        pool_u.create(s, int(lens[s]))
+    tab_u, _ = pool_u.tables(list(range(B)), mb)
+    slots_u = np.concatenate([np.asarray(pool_u.slots(s, 0, int(lens[s])), np.int64) for s in range(B)])
+    pool_u.close()
+    cu_full = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    suf_cu = plan.suffix_cu
+    qp, kp, vp = dev_t(plan.prefix_q), dev_t(plan.prefix_k), dev_t(plan.prefix_v)
+    qf = torch.cat([x for s in range(B) for x in (qp, q[suf_cu[s]:suf_cu[s + 1]])])
+    kf = torch.cat([x for s in range(B) for x in (kp, kn[suf_cu[s]:suf_cu[s + 1]])])
+    vf = torch.cat([x for s in range(B) for x in (vp, vn[suf_cu[s]:suf_cu[s + 1]])])
+    out_f = torch.empty_like(qf)
+    steps_u = [(pkv.prepare_write_kv(kf, vf, dev_t(slots_u), kc, vc),
+                pkv.prepare_prefill(qf, kc, vc, dev_t(tab_u), ctx_d, dev_t(cu_full), int(lens.max()),
+                                    int(lens.max()), plan.scale, out_f))]
+    step_u, prefill_u = timed(steps_u, 1)
+
+    prompt_tokens = int(lens.sum())
+    computed = int(plan.suffix_lens.sum())
+    flops = causal_flops(lens, plan.suffix_cu, plan.num_q_heads, plan.head_dim)
+    achieved = flops / prefill_s / 1e12
+    result = {
+        "metric": PREFIX_METRIC,
+        "value": round(prompt_tokens / step_s, 1),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded token ids, shuffled block placement)",
+        "config": {"workload": args.workload, "requests_per_step": B, "system_prompt_tokens": plan.prefix_len,
+                   "suffix_tokens_min": int(plan.suffix_lens.min()), "suffix_tokens_max": int(plan.suffix_lens.max()),
+                   "prompt_tokens_per_step": prompt_tokens, "computed_tokens_per_step": computed,
+                   "num_q_heads": plan.num_q_heads, "num_kv_heads": plan.num_kv_heads,
+                   "head_dim": plan.head_dim, "block_size": bs},
+        "cache_hit_fraction": round(cached_tokens / (nsteps * prompt_tokens), 4),
+        "host_manager_us_per_request": round(host_s / (nsteps * B) * 1e6, 2),
+        "uncached_tokens_per_s": round(prompt_tokens / step_u, 1),
+        "uncached_ms_per_step": round(step_u * 1e3, 5),
+        "speedup_vs_uncached": round(step_u / step_s, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel", "avg_launch_us": round(prefill_s * 1e6, 2),
+                     "algorithmic_flops_per_launch": flops,
+                     "uncached_avg_launch_us": round(prefill_u * 1e6, 2)},
+        "cpu_baseline": None,
+    }
+    pool.close()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        result["cpu_baseline"] = prefix_cpu_baseline(plan, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def waste_main(args):
+    """Host-only: the serving-loop simulation of both allocators, timed."""
+    import paged_kv_cache_354_amd as pkv
+
+    case = WASTE_WORKLOADS[args.workload]()
+    args_c = (case.capacity, case.block_size, case.prompt_lens, case.output_lens, case.reserve_lens)
+    res, secs = {}, {}
+    for mode in ("contiguous", "paged"):
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            res[mode] = pkv.pa_waste_simulate(mode, *args_c)
+        secs[mode] = (time.perf_counter() - t0) / args.steps
+
+    def summary(st):
+        return {"waste_pct": round(100.0 * (1 - st["live_slot_steps"] / st["held_slot_steps"]), 3),
+                "mean_running": round(st["running_steps"] / st["steps"], 2), "max_running": st["max_running"],
+                "steps": st["steps"], "tokens_per_step": round(st["decode_tokens"] / st["steps"], 2),
+                "preemptions": st["preemptions"], "frag_blocked_steps": st["frag_blocked_steps"]}
+
+    c, pg = summary(res["contiguous"]), summary(res["paged"])
+    result = {
+        "metric": WASTE_METRIC, "value": pg["waste_pct"], "unit": "%",
+        "n_gpus": 1, "steps": args.steps, "warmup": 0,
+        "ms_per_step": round(secs["paged"] * 1e3, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int64",
+        "data": "synthetic (seeded request lengths)",
+        "config": {"workload": args.workload, "requests": len(case.prompt_lens), "capacity_slots": case.capacity,
+                   "block_size": case.block_size, "prompt_tokens_mean": round(float(case.prompt_lens.mean()), 1),
+                   "output_tokens_mean": round(float(case.output_lens.mean()), 1),
+                   "slab_slots_mean": round(float(case.reserve_lens.mean()), 1)},
+        "paged": pg, "contiguous": c,
+        "concurrency_gain": round(pg["mean_running"] / c["mean_running"], 3),
+        "makespan_ratio_contiguous_over_paged": round(c["steps"] / pg["steps"], 3),
+        "sim_seconds": {k: round(v, 4) for k, v in secs.items()},
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        from oracle import waste as WS
+
+        k = 64  # about 20 s of the oracle (its manager model copies its state on every call)
+        small = case.scaled(k)
+        t0 = time.perf_counter()
+        st = WS.simulate("paged", small.capacity, small.block_size, small.prompt_lens, small.output_lens,
+                         small.reserve_lens)
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        result["cpu_baseline"] = {
+            "value": round(100.0 * st.waste(), 3), "unit": "%", "cores": int(threads), "kind": "oracle",
+            "sample": f"the oracle's paged run on 1/{k} of the requests and of the pool "
+                      f"({len(small.prompt_lens)} requests, {small.capacity} slots), {dt:.2f} s wall",
+            "seconds": round(dt, 2)}
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 # --- main ------------------------------------------------------------------------------
 
 def main(argv=None):
@@ -439,6 +704,9 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+
+    if args.workload in WASTE_WORKLOADS:
+        return waste_main(args)
 
     import torch
 
@@ -453,6 +721,8 @@ def main(argv=None):
         return prefill_main(args, torch, pkv, dev)
     if args.workload in SWAP_WORKLOADS:
         return swap_main(args, torch, pkv, dev)
+    if args.workload in PREFIX_WORKLOADS:
+        return prefix_main(args, torch, pkv, dev)
     make, default_part = WORKLOADS[args.workload]
     partition = default_part if args.partition is None else args.partition
 

@@ -106,7 +106,7 @@ def simulate(mode, capacity, block_size, prompt_lens, output_lens, reserve_lens)
     length = {}           # request -> tokens stored
     slab = {}             # request -> slab start (contiguous)
     gaps = [(0, capacity)] if capacity else []
-    pool = BlockManagerModel(num_blocks, block_size) if mode == PAGED else None
+    pool = BlockManagerModel(num_blocks, block_size) if mode == PAGED and n else None  # no requests: no pool
 
     while waiting or running:
         # admission, first come first served

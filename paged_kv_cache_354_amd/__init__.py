@@ -64,6 +64,17 @@ _lib = None
 _i32, _i64, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 _P32, _P64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
 
+
+class WasteStats(ctypes.Structure):
+    """pa_waste_stats: integer totals of one simulated serving run."""
+
+    _fields_ = [(n, ctypes.c_int64) for n in ("steps", "live_slot_steps", "held_slot_steps", "running_steps",
+                                              "max_running", "preemptions", "frag_blocked_steps",
+                                              "decode_tokens")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
 _SIGS = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_last_error": (ctypes.c_char_p, []),
@@ -103,6 +114,7 @@ _SIGS = {
     "pa_pool_is_cached": (_i32, [_vp, _i32]),
     "pa_pool_lru_list": (_i32, [_vp, _P32, _i32, _P32]),
     "pa_seq_create_cached": (_i32, [_vp, _i64, _P32, _i32, _P32]),
+    "pa_waste_simulate": (_i32, [_i32, _i64, _i32, _P32, _P32, _P32, _i32, ctypes.POINTER(WasteStats)]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -482,6 +494,24 @@ def pa_seq_create_cached(pool, seq, tokens):
     ptr = _np_ptr(t, ctypes.c_int32) if t.size else None
     _check(load().pa_seq_create_cached(pool, seq, ptr, int(t.size), ctypes.byref(got)))
     return got.value
+
+
+PA_WASTE_CONTIGUOUS, PA_WASTE_PAGED = 0, 1
+
+
+def pa_waste_simulate(mode, capacity, block_size, prompt_lens, output_lens, reserve_lens):
+    """Serving loop over one pool of ``capacity`` KV slots; ``mode`` is
+    "contiguous" or "paged".  Returns the totals as a dict."""
+    m = {"contiguous": PA_WASTE_CONTIGUOUS, "paged": PA_WASTE_PAGED}[mode]
+    arrs = [np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+            for a in (prompt_lens, output_lens, reserve_lens)]
+    n = arrs[0].size
+    if any(a.size != n for a in arrs):
+        raise PagedKVError(PA_EINVAL, "prompt, output and reserve lengths differ in count")
+    ptrs = [_np_ptr(a, ctypes.c_int32) if n else None for a in arrs]
+    st = WasteStats()
+    _check(load().pa_waste_simulate(m, int(capacity), int(block_size), *ptrs, n, ctypes.byref(st)))
+    return st.as_dict()
 
 
 def pa_seq_create(pool, seq, num_tokens):

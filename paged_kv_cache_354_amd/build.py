@@ -18,6 +18,7 @@ LIB = os.path.join(HERE, "libpagedkv.so")
 SOURCES = [
     "csrc/pa_status.cpp",
     "csrc/block_manager.cpp",
+    "csrc/waste_sim.cpp",
     "csrc/pa_cache_ops.hip",
     "csrc/pa_decode.hip",
     "csrc/pa_decode_gqa.hip",

@@ -390,6 +390,127 @@ def c4_shared_prefix(seed=4, num_seqs=256, prefix_len=2048, suffix_hi=512, steps
                             suffix_lens=suffix, suffix_k=sk, suffix_v=sv, rng=rng)
 
 
+# --- prefix-cached prompt admission ------------------------------------------
+
+@dataclass
+class CachedPromptsPlan:
+    """Inputs of the prefix-cached prompt workload.
+
+    Every step admits ``num_seqs`` new requests whose prompts are one shared
+    ``prefix_len``-token system prompt followed by a private suffix of
+    ``suffix_lens[s]`` tokens (the same lengths every step, fresh token ids,
+    so only the system prompt can be found in the cache).  Token ids are
+    int32; K/V/q rows are token-major ``[n][heads][d]``.  Queries and K/V of
+    the prefix are drawn once (the same tokens give the same KV); those of
+    each request's suffix are drawn per request and reused by every step.
+    """
+
+    dtype: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    prefix_len: int
+    num_blocks: int
+    scale: float
+    free_order: np.ndarray
+    prefix_tokens: np.ndarray  # int32 [prefix_len]
+    suffix_lens: np.ndarray    # int32 [B]
+    prefix_q: np.ndarray       # [prefix_len][Hq][d]
+    prefix_k: np.ndarray       # [prefix_len][Hkv][d]
+    prefix_v: np.ndarray
+    suffix_q: np.ndarray       # [sum suffix_lens][Hq][d], request after request
+    suffix_k: np.ndarray       # [sum suffix_lens][Hkv][d]
+    suffix_v: np.ndarray
+
+    @property
+    def suffix_cu(self):
+        return np.concatenate([[0], np.cumsum(self.suffix_lens)]).astype(np.int32)
+
+    def prompt(self, step, s):
+        """Token ids of request ``s`` admitted at ``step``: the system prompt,
+        then ids no other (step, request) uses."""
+        n = int(self.suffix_lens[s])
+        base = 1 << 20  # above every system-prompt id
+        uniq = base + ((step * self.num_seqs + s) * 1024 + np.arange(n)) % ((1 << 31) - base)
+        return np.concatenate([self.prefix_tokens, uniq.astype(np.int32)]).astype(np.int32)
+
+
+def c8_prefix_cached_prompts(seed=8, num_seqs=64, prefix_len=2048, suffix_lo=64, suffix_hi=512,
+                             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, dtype=BF16):
+    """Llama-3-8B-shaped prompt admission with a cached 2048-token system
+    prompt: 64 requests per step, private suffixes of U{64..512} tokens."""
+    rng = np.random.default_rng(seed)
+    suffix = rng.integers(suffix_lo, suffix_hi, size=num_seqs, endpoint=True).astype(np.int32)
+    prefix_tokens = rng.integers(0, 1 << 20, size=prefix_len).astype(np.int32)
+    # the uncached comparison holds every prompt privately
+    need = sum(ceil_div(prefix_len + int(n), block_size) for n in suffix)
+    num_blocks = int(np.ceil(1.25 * need))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    t = int(suffix.sum())
+    return CachedPromptsPlan(
+        dtype=dtype, num_seqs=num_seqs, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        block_size=block_size, prefix_len=prefix_len, num_blocks=num_blocks,
+        scale=float(np.float32(1.0 / np.sqrt(head_dim))), free_order=free_order, prefix_tokens=prefix_tokens,
+        suffix_lens=suffix,
+        prefix_q=normal(rng, (prefix_len, num_q_heads, head_dim), dtype),
+        prefix_k=normal(rng, (prefix_len, num_kv_heads, head_dim), dtype),
+        prefix_v=normal(rng, (prefix_len, num_kv_heads, head_dim), dtype),
+        suffix_q=normal(rng, (t, num_q_heads, head_dim), dtype),
+        suffix_k=normal(rng, (t, num_kv_heads, head_dim), dtype),
+        suffix_v=normal(rng, (t, num_kv_heads, head_dim), dtype))
+
+
+# --- KV waste of a serving loop ----------------------------------------------
+
+# One MI355X serving Llama-3-8B in bf16: 288 GB of HBM, 90% of it for the
+# engine (the glossary entry's launch example), minus the 8.03e9 bf16 weights;
+# each token's KV is 32 layers x (K + V) x 8 heads x 128 x 2 bytes.
+LLAMA3_8B_KV_BYTES_PER_TOKEN = 32 * 2 * 8 * 128 * 2
+MI355X_KV_CAPACITY_SLOTS = int((0.90 * 288e9 - 8.03e9 * 2) // LLAMA3_8B_KV_BYTES_PER_TOKEN)
+
+
+@dataclass
+class WasteCase:
+    """Requests of one serving run: prompt ``p``, generated tokens ``o`` and
+    contiguous slab ``r = p + max_tokens`` (the longest output the request
+    may produce), all int32 [n]."""
+
+    name: str
+    capacity: int
+    block_size: int
+    prompt_lens: np.ndarray
+    output_lens: np.ndarray
+    reserve_lens: np.ndarray
+
+    def scaled(self, k):
+        """The first n / k requests on a pool k times smaller (a bounded sample)."""
+        n = max(1, len(self.prompt_lens) // k)
+        cap = max(self.capacity // k, int(self.reserve_lens[:n].max()))
+        return WasteCase(f"{self.name}/{k}", cap, self.block_size, self.prompt_lens[:n], self.output_lens[:n],
+                         self.reserve_lens[:n])
+
+
+def waste_case(name="waste_llama3_8b_c2", seed=9, num_requests=4096, capacity=None, block_size=16,
+               max_tokens_choices=(256, 512, 1024, 2048)):
+    """Prompts from the decode workloads' length mixes (``_c2``: U{128..4096};
+    ``_c5``: lognormal, median 600, sigma 1, clipped to [16, 4096]); each
+    request's max_tokens drawn from ``max_tokens_choices`` and its output
+    length from U{1..max_tokens} (requests stop early)."""
+    rng = np.random.default_rng(seed)
+    if name.endswith("_c2"):
+        p = rng.integers(128, 4096, size=num_requests, endpoint=True)
+    elif name.endswith("_c5"):
+        p = c5_lengths(rng, num_requests, hi=4096)
+    else:
+        raise ValueError(name)
+    m = rng.choice(np.asarray(max_tokens_choices), size=num_requests)
+    o = rng.integers(1, m, endpoint=True)
+    cap = MI355X_KV_CAPACITY_SLOTS if capacity is None else capacity
+    return WasteCase(name, int(cap), block_size, p.astype(np.int32), o.astype(np.int32), (p + m).astype(np.int32))
+
+
 CONFIGS = {
     "tiny_f32": c1_tiny_f32,
     "llama3_8b_b64": c2_llama8b_b64,
