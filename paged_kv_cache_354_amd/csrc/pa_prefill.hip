@@ -7,19 +7,22 @@
 // them through the table; a prompt is many tokens at once.  The attention is
 // the textbook causal softmax: the query at position p sees keys 0..p.)
 //
-// One workgroup (4 wave64s) takes 16 query tokens of GW = min(G, 4) query
-// heads of one KV head (for G < 4, 4 / G blocks of 16 tokens), so that the
-// key/value tiles it stages in LDS serve 64 (token, head) rows.  Per tile of
-// 32 keys every wave computes, on the matrix cores (v_mfma_f32_16x16x32_bf16):
+// One workgroup (4 wave64s) takes 32 query tokens of GW = min(G, 4) query
+// heads of one KV head (for G < 4, 4 / G blocks of 32 tokens), so that the
+// key/value tiles it stages in LDS serve 128 (token, head) rows.  A wave
+// owns 32 rows of one head, as two blocks of 16, and every K or V^T operand
+// it reads from LDS feeds both blocks.  Per tile of 32 keys each block
+// computes, on the matrix cores (v_mfma_f32_16x16x32_bf16):
 //
-//   S^T = K Q^T       keys in M, the wave's 16 query rows in N, channels in K.
-//                     Lane (g, n) ends up with the scores of row n for keys
-//                     4g..4g+3 of each 16-key half.
+//   S^T = K Q^T       keys in M, the block's 16 query rows in N, channels in
+//                     K.  Lane (g, n) ends up with the scores of row n for
+//                     keys 4g..4g+3 of each 16-key half.
 //   O^T += V^T P^T    channels in M (16 per block), rows in N, the 32 keys in
 //                     K.  The lane's 8 probabilities (keys 4g..4g+3 and
 //                     16+4g..16+4g+3, its own S^T entries rounded to bf16)
-//                     are exactly its B operand, so no value crosses lanes;
-//                     the A operand reads V^T from LDS in that key order.
+//                     are exactly its B operand, so no value crosses lanes.
+//                     V^T rows sit in LDS in that key order, so the lane's
+//                     A operand is one 16-byte read.
 //
 // Every O^T value a lane holds belongs to its own row n, so the online
 // softmax rescale is lane-local; only the row max and the final row sum are
@@ -51,7 +54,8 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;  // 4 wave64s
 constexpr int kKeys = 32;      // keys per tile
-constexpr int kVtWords = 17;   // 32-bit words per V^T row in LDS: 16 key pairs + 1 (bank spread)
+constexpr int kRB = 2;         // 16-row blocks per wave
+constexpr int kVtChunks = 5;   // 16-byte chunks per V^T row in LDS: 4 of keys + 1 (bank spread)
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
@@ -73,22 +77,28 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t ctx_cap;   // lengths are clamped to this
-  int32_t q_blocks;  // query blocks per sequence in the grid
+  int32_t q_blocks;  // query blocks (of the workgroup's tokens) per sequence in the grid
   int32_t out_f32;   // 1: fp32 output, 0: bf16
   float qscale;      // scale * log2(e)
 };
 
+// V^T row layout: chunk c (16 bytes) of a channel's row holds keys 4c..4c+3
+// then 16+4c..16+4c+3, the 8 keys lane group c multiplies.
+__device__ __forceinline__ int vt_word(int key) {  // 32-bit word of a key pair (key even)
+  return 4 * ((key & 15) >> 2) + 2 * (key >> 4) + ((key & 3) >> 1);
+}
+
 template <int D>
 struct PrefillShared {
   uint4 k[2][kKeys][D / 8 + 1];        // K rows of the tile (double buffer), 16 B of padding per row
-  uint32_t vt[2][D][kVtWords];         // V^T of the tile: bf16 key pairs per 32-bit word
+  uint4 vt[2][D][kVtChunks];           // V^T of the tile, keys in lane order (vt_word)
   int32_t tbl[kTblLds];                // block ids of keys [0, kend)
 };
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   constexpr int GW = G < 4 ? G : 4;   // query heads per workgroup
-  constexpr int TQ = 16 * (4 / GW);   // query tokens per workgroup
+  constexpr int TQ = 16 * kRB * (4 / GW);  // query tokens per workgroup
   constexpr int HG = G / GW;          // workgroups per (KV head, query block)
   constexpr int C = D / 8;            // 16-byte chunks per row
   constexpr int KSTEPS = D / 32;
@@ -96,17 +106,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared<D> sh;
 
   // Work order: query block (last first: causal blocks near the end see the
-  // most keys), head group, KV head, sequence; contiguous ranges per XCD, so
-  // the workgroups an XCD runs together read the same (sequence, KV head)
-  // keys and values from its L2.
+  // most keys), sequence, head group, KV head; contiguous ranges per XCD.
+  // With the KV head slowest, XCD x takes the same KV head(s) of every
+  // sequence: the XCDs get equal shares however unequal the sequences are,
+  // and an XCD's L2 holds the keys and values of its own heads only.
   const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
   int r = xcd_work_id(blockIdx.x, n_work);
   const int qb = a.q_blocks - 1 - r % a.q_blocks;
   r /= a.q_blocks;
+  const int s = r % a.num_seqs;
+  r /= a.num_seqs;
   const int hg = r % HG;
-  r /= HG;
-  const int kvh = r % a.num_kv_heads;
-  const int s = r / a.num_kv_heads;
+  const int kvh = r / HG;
 
   const int lo = a.cu_seqlens[s];
   const int n = a.cu_seqlens[s + 1] - lo;
@@ -122,28 +133,38 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int g = lane >> 4;
   const int nl = lane & 15;
   const int h = kvh * G + hg * GW + wave % GW;
-  const int tok0 = q0 + (wave / GW) * 16;  // the wave's first query
+  const int tok0 = q0 + (wave / GW) * 16 * kRB;  // the wave's first query
   // keys the workgroup needs, and the ones this wave needs
   const int kend = max(0, min(ctx, first_pos + min(q0 + TQ, n)));
-  const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16, n))) : 0;
+  const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16 * kRB, n))) : 0;
 
-  // The lane's row (query tok, head h) and its last visible key.
-  const int tok = tok0 + nl;
-  const bool row_ok = tok < n;
-  const int prow = row_ok ? first_pos + tok : -1;
-
-  // B operand of S^T: channels [8(4i + g), +8) of the row's query.
-  uint4 qop[KSTEPS];
-  {
-    const uint4 *qrow = a.q + ((size_t)(lo + (row_ok ? tok : 0)) * a.num_q_heads + h) * C + g;
+  // The lane's rows (query tok0 + 16r + nl, head h) and their last visible keys.
+  int prow[kRB];
+  bool row_ok[kRB];
+  // B operands of S^T: channels [8(4i + g), +8) of each row's query.
+  uint4 qop[kRB][KSTEPS];
 #pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) qop[i] = row_ok ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int tok = tok0 + 16 * rb + nl;
+    row_ok[rb] = tok < n;
+    prow[rb] = row_ok[rb] ? first_pos + tok : -1;
+    const uint4 *qrow = a.q + ((size_t)(lo + (row_ok[rb] ? tok : 0)) * a.num_q_heads + h) * C + g;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) qop[rb][i] = row_ok[rb] ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
   }
 
-  f32x4_t o[OB];  // O^T: channel 16j + 4g + e of row nl
+  f32x4_t o[kRB][OB];  // O^T: channel 16j + 4g + e of row nl of block rb
 #pragma unroll
-  for (int j = 0; j < OB; ++j) o[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = kNegBig, l = 0.0f;  // running max (shared by the row's 4 lanes) and this lane's sum
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int j = 0; j < OB; ++j) o[rb][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // running max per row (shared by the row's 4 lanes) and this lane's sum
+  float m[kRB], l[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m[rb] = kNegBig;
+    l[rb] = 0.0f;
+  }
 
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
   const size_t block_rows = (size_t)a.num_kv_heads * a.block_size;
@@ -213,10 +234,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       // V^T: channel 8ch + c gets the word (key 2kp, key 2kp + 1)
       const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
       const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+      const int wd = vt_word(2 * kp);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        sh.vt[b][8 * ch + 2 * c][kp] = (w0[c] & 0xffffu) | (w1[c] << 16);
-        sh.vt[b][8 * ch + 2 * c + 1][kp] = (w0[c] >> 16) | (w1[c] & 0xffff0000u);
+        reinterpret_cast<uint32_t *>(sh.vt[b][8 * ch + 2 * c])[wd] = (w0[c] & 0xffffu) | (w1[c] << 16);
+        reinterpret_cast<uint32_t *>(sh.vt[b][8 * ch + 2 * c + 1])[wd] = (w0[c] >> 16) | (w1[c] & 0xffff0000u);
       }
     }
   };
@@ -235,60 +257,82 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     const int kt0 = t * kKeys;
     if (t + 1 < ntiles) load_tile(kt0 + kKeys);  // in flight during this tile's math
     if (kt0 < wkend) {
-      // S^T for the two 16-key halves.
-      f32x4_t st[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        st[hh] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < KSTEPS; ++i)
-          st[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, sh.k[b][16 * hh + nl][4 * i + g]),
-                                                           __builtin_bit_cast(bf16x8_t, qop[i]), st[hh], 0, 0, 0);
-      }
-      // Causal mask, running max over the row's 4 lanes, probabilities.
-      float z[8];
-      float mx = -INFINITY;
+      // S^T for the two 16-key halves of both row blocks; each K operand
+      // read from LDS feeds both blocks.
+      // All K operands are read before the first product, so their LDS
+      // latencies overlap instead of adding up.
+      bf16x8_t kop[2][KSTEPS];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kt0 + 16 * hh + 4 * g + e;
-          const float v = key <= prow ? st[hh][e] * a.qscale : -INFINITY;
-          z[4 * hh + e] = v;
-          mx = fmaxf(mx, v);
+        for (int i = 0; i < KSTEPS; ++i) kop[hh][i] = __builtin_bit_cast(bf16x8_t, sh.k[b][16 * hh + nl][4 * i + g]);
+      f32x4_t st[kRB][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) st[rb][hh] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < KSTEPS; ++i)
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+            st[rb][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[hh][i], __builtin_bit_cast(bf16x8_t, qop[rb][i]),
+                                                                 st[rb][hh], 0, 0, 0);
+      }
+      // The V^T operands (chunk g of each channel's row) are read now, so
+      // that they arrive during the softmax.
+      bf16x8_t vop[OB];
+#pragma unroll
+      for (int j = 0; j < OB; ++j) vop[j] = __builtin_bit_cast(bf16x8_t, sh.vt[b][16 * j + nl][g]);
+      // Per row block: causal mask (only where the tile reaches past the
+      // block's first row), reference max, probabilities.
+      bf16x8_t pb[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const bool diag = kt0 + kKeys - 1 > first_pos + tok0 + 16 * rb;  // wave-uniform
+        float z[8];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt0 + 16 * hh + 4 * g + e;
+            float v = st[rb][hh][e] * a.qscale;
+            if (diag) v = key <= prow[rb] ? v : -INFINITY;
+            z[4 * hh + e] = v;
+            mx = fmaxf(mx, v);
+          }
+        // The reference max m moves only when some score passes it by more
+        // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
+        // 2^kLazyMax, and the rescale of O^T is rare after the first tiles.
+        // The test needs only this lane's max; inside, every row takes the
+        // max over its 4 lanes, so the 4 lanes of a row keep one m.  The
+        // result does not depend on m.
+        if (__any(mx > m[rb] + kLazyMax)) {
+          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mn = fmaxf(m[rb], mx);
+          const float alpha = exp2_fast(m[rb] - mn);
+          m[rb] = mn;
+          l[rb] *= alpha;
+#pragma unroll
+          for (int j = 0; j < OB; ++j) o[rb][j] *= alpha;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // The reference max m moves only when a row's scores pass it by more
-      // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
-      // 2^kLazyMax, and the rescale of O^T (held in matrix-core registers)
-      // is rare after the first tiles.  The result does not depend on m.
-      if (__any(mx > m + kLazyMax)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = exp2_fast(m - mn);
-        m = mn;
-        l *= alpha;
+        f32x8_t p;
+        float ps = 0.0f;
 #pragma unroll
-        for (int j = 0; j < OB; ++j) o[j] *= alpha;
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2_fast(z[e] - m[rb]);
+          ps += p[e];
+        }
+        l[rb] += ps;
+        pb[rb] = __builtin_convertvector(p, bf16x8_t);
       }
-      f32x8_t p;
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = exp2_fast(z[e] - m);
-        ps += p[e];
-      }
-      l += ps;
-      const bf16x8_t pb = __builtin_convertvector(p, bf16x8_t);
       // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
 #pragma unroll
-      for (int j = 0; j < OB; ++j) {
-        const uint32_t *vr = &sh.vt[b][16 * j + nl][0];  // key pairs
-        // keys 4g .. 4g + 3, then 16 + 4g .. 16 + 4g + 3 (rows are 17 words:
-        // 4-byte reads only)
-        const uint4 av = make_uint4(vr[2 * g], vr[2 * g + 1], vr[8 + 2 * g], vr[9 + 2 * g]);
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pb, o[j], 0, 0, 0);
-      }
+      for (int j = 0; j < OB; ++j)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+          o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[j], pb[rb], o[rb][j], 0, 0, 0);
     }
     if (t + 1 < ntiles) store_tile(b ^ 1, kt0 + kKeys);
     __syncthreads();
@@ -298,20 +342,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   else run(std::false_type{});
 
   // Row sums over the row's 4 lanes; normalised output.
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
-  if (row_ok) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const size_t base = ((size_t)(lo + tok) * a.num_q_heads + h) * D + 4 * g;
 #pragma unroll
-    for (int j = 0; j < OB; ++j) {
-      const f32x4_t v = o[j] * inv;
-      if (a.out_f32) {
-        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + 16 * j) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        const uint32_t w0 = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
-        const uint32_t w1 = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base + 16 * j) = make_uint2(w0, w1);
+  for (int rb = 0; rb < kRB; ++rb) {
+    float lr = l[rb];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    if (row_ok[rb]) {
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+      const size_t base = ((size_t)(lo + tok0 + 16 * rb + nl) * a.num_q_heads + h) * D + 4 * g;
+#pragma unroll
+      for (int j = 0; j < OB; ++j) {
+        const f32x4_t v = o[rb][j] * inv;
+        if (a.out_f32) {
+          *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + 16 * j) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          const uint32_t w0 = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
+          const uint32_t w1 = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base + 16 * j) = make_uint2(w0, w1);
+        }
       }
     }
   }
@@ -371,7 +420,7 @@ extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num
   while ((1 << log2_bs) < c.block_size) ++log2_bs;
   const int64_t cap64 = (int64_t)max_blocks_per_seq * c.block_size;
   const int gw = g < 4 ? g : 4;
-  const int tq = 16 * (4 / gw);
+  const int tq = 16 * kRB * (4 / gw);
   PrefillArgs a{};
   a.q = (const uint4 *)q;
   a.k_cache = (const uint4 *)k_cache;
