@@ -21,8 +21,12 @@
 //                     K.  The lane's 8 probabilities (keys 4g..4g+3 and
 //                     16+4g..16+4g+3, its own S^T entries rounded to bf16)
 //                     are exactly its B operand, so no value crosses lanes.
-//                     V^T rows sit in LDS in that key order, so the lane's
-//                     A operand is one 16-byte read.
+//                     V stays in LDS as key rows; the A operand (V^T) comes
+//                     from two transposing LDS reads (ds_read_b64_tr_b16):
+//                     in each 16-lane group, lane i names 4 channels of one
+//                     key row and lane 4a + e receives channel e of the rows
+//                     named by lanes a, a + 4, a + 8, a + 12, so lane n gets
+//                     channel n of 4 key rows.
 //
 // Every O^T value a lane holds belongs to its own row n, so the online
 // softmax rescale is lane-local; only the row max and the final row sum are
@@ -55,7 +59,6 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;  // 4 wave64s
 constexpr int kKeys = 32;      // keys per tile
 constexpr int kRB = 2;         // 16-row blocks per wave
-constexpr int kVtChunks = 5;   // 16-byte chunks per V^T row in LDS: 4 of keys + 1 (bank spread)
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
@@ -82,16 +85,14 @@ struct PrefillArgs {
   float qscale;      // scale * log2(e)
 };
 
-// V^T row layout: chunk c (16 bytes) of a channel's row holds keys 4c..4c+3
-// then 16+4c..16+4c+3, the 8 keys lane group c multiplies.
-__device__ __forceinline__ int vt_word(int key) {  // 32-bit word of a key pair (key even)
-  return 4 * ((key & 15) >> 2) + 2 * (key >> 4) + ((key & 3) >> 1);
-}
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 template <int D>
 struct PrefillShared {
   uint4 k[2][kKeys][D / 8 + 1];        // K rows of the tile (double buffer), 16 B of padding per row
-  uint4 vt[2][D][kVtChunks];           // V^T of the tile, keys in lane order (vt_word)
+  uint4 v[2][kKeys][D / 8 + 2];        // V rows of the tile, 32 B of padding per row: the 4 rows a
+                                       // transposing read spans start in different bank groups
   int32_t tbl[kTblLds];                // block ids of keys [0, kend)
 };
 
@@ -230,15 +231,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         kv[e] = live ? kreg[u][e] : make_uint4(0, 0, 0, 0);
         vv[e] = live ? vreg[u][e] : make_uint4(0, 0, 0, 0);
         sh.k[b][2 * kp + e][ch] = kv[e];
-      }
-      // V^T: channel 8ch + c gets the word (key 2kp, key 2kp + 1)
-      const uint32_t w0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
-      const uint32_t w1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
-      const int wd = vt_word(2 * kp);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        reinterpret_cast<uint32_t *>(sh.vt[b][8 * ch + 2 * c])[wd] = (w0[c] & 0xffffu) | (w1[c] << 16);
-        reinterpret_cast<uint32_t *>(sh.vt[b][8 * ch + 2 * c + 1])[wd] = (w0[c] >> 16) | (w1[c] & 0xffff0000u);
+        sh.v[b][2 * kp + e][ch] = vv[e];
       }
     }
   };
@@ -278,11 +271,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
             st[rb][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[hh][i], __builtin_bit_cast(bf16x8_t, qop[rb][i]),
                                                                  st[rb][hh], 0, 0, 0);
       }
-      // The V^T operands (chunk g of each channel's row) are read now, so
-      // that they arrive during the softmax.
+      // The V^T operands are read now, so that they arrive during the
+      // softmax: for channel block j, lane (g, n) names key rows
+      // 4g + n / 4 and 16 + 4g + n / 4 at channels 16j + 4 (n % 4) .. + 3,
+      // and receives channel 16j + n of keys 4g..4g+3 and 16+4g..16+4g+3.
       bf16x8_t vop[OB];
+      {
+        constexpr int VS = D + 16;  // elements per V row in LDS
+        const uint16_t *vb = reinterpret_cast<const uint16_t *>(&sh.v[b][0][0]);
+        const int off0 = (4 * g + (nl >> 2)) * VS + 4 * (nl & 3);
 #pragma unroll
-      for (int j = 0; j < OB; ++j) vop[j] = __builtin_bit_cast(bf16x8_t, sh.vt[b][16 * j + nl][g]);
+        for (int j = 0; j < OB; ++j) {
+          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * j));
+          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * VS + 16 * j));
+          vop[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
       // Per row block: causal mask (only where the tile reaches past the
       // block's first row), reference max, probabilities.
       bf16x8_t pb[kRB];
