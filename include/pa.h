@@ -250,6 +250,7 @@ pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_ma
  *   block_tables, max_blocks_per_seq, max_context_len: as for pa_decode
  *                 (lengths are clamped to min(max_context_len,
  *                 max_blocks_per_seq * block_size)).
+ *   scale         the softmax scale; positive and finite, else PA_EINVAL.
  *   out           device [num_tokens][num_q_heads][head_dim] of out_dtype
  *                 (PA_F32 or PA_BF16).
  * Built for bf16 pools, head_dim 64 or 128, 1, 2, 4 or 8 query heads per KV

@@ -201,37 +201,47 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     else blk = max(0, min(trow[kk >> a.log2_bs], a.num_blocks - 1));
     return (size_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
   };
+  // A tile below kend needs neither the clamp nor the zero fill; the two
+  // keys of a pair share a block (and sit in consecutive rows) unless the
+  // block size is 1.
+  const bool pair_rows = a.block_size >= 2;
   auto load_tile = [&](int kt0) {
+    const bool full = kt0 + kKeys <= kend;  // uniform
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int item = tid + u * kThreads;
       if (item >= ITEMS) break;  // uniform per wave
       const int ch = item % C;
       const int kp = item / C;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int kk = min(kt0 + 2 * kp + e, kend - 1);
-        const size_t row = key_row(kk);
-        kreg[u][e] = a.k_cache[row * C + ch];
-        vreg[u][e] = load_stream(a.v_cache + row * C + ch);
+      const int k0 = kt0 + 2 * kp;
+      size_t o0, o1;  // uint4 offsets of the two keys' chunks
+      if (full) {
+        o0 = key_row(k0) * C + ch;
+        o1 = pair_rows ? o0 + C : key_row(k0 + 1) * C + ch;
+      } else {
+        o0 = key_row(min(k0, kend - 1)) * C + ch;
+        o1 = key_row(min(k0 + 1, kend - 1)) * C + ch;
       }
+      kreg[u][0] = a.k_cache[o0];
+      kreg[u][1] = a.k_cache[o1];
+      vreg[u][0] = load_stream(a.v_cache + o0);
+      vreg[u][1] = load_stream(a.v_cache + o1);
     }
   };
   auto store_tile = [&](int b, int kt0) {
+    const bool full = kt0 + kKeys <= kend;  // uniform
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int item = tid + u * kThreads;
       if (item >= ITEMS) break;  // uniform per wave
       const int ch = item % C;
       const int kp = item / C;
-      uint4 kv[2], vv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const bool live = kt0 + 2 * kp + e < kend;
-        kv[e] = live ? kreg[u][e] : make_uint4(0, 0, 0, 0);
-        vv[e] = live ? vreg[u][e] : make_uint4(0, 0, 0, 0);
-        sh.k[b][2 * kp + e][ch] = kv[e];
-        sh.v[b][2 * kp + e][ch] = vv[e];
+        uint4 kv = kreg[u][e], vv = vreg[u][e];
+        if (!full && kt0 + 2 * kp + e >= kend) kv = vv = make_uint4(0, 0, 0, 0);
+        sh.k[b][2 * kp + e][ch] = kv;
+        sh.v[b][2 * kp + e][ch] = vv;
       }
     }
   };
@@ -293,6 +303,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         const bool diag = kt0 + kKeys - 1 > first_pos + tok0 + 16 * rb;  // wave-uniform
+        // raw scores; the scale (positive) enters through the max and the
+        // exponent's fma
         float z[8];
         float mx = -INFINITY;
 #pragma unroll
@@ -300,11 +312,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = kt0 + 16 * hh + 4 * g + e;
-            float v = st[rb][hh][e] * a.qscale;
+            float v = st[rb][hh][e];
             if (diag) v = key <= prow[rb] ? v : -INFINITY;
             z[4 * hh + e] = v;
             mx = fmaxf(mx, v);
           }
+        mx *= a.qscale;
         // The reference max m moves only when some score passes it by more
         // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
         // 2^kLazyMax, and the rescale of O^T is rare after the first tiles.
@@ -323,9 +336,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         }
         f32x8_t p;
         float ps = 0.0f;
+        const float negm = -m[rb];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2_fast(z[e] - m[rb]);
+          p[e] = exp2_fast(fmaf(z[e], a.qscale, negm));
           ps += p[e];
         }
         l[rb] += ps;
@@ -411,6 +425,8 @@ extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num
   if (num_q_heads % c.num_kv_heads)
     return fail(PA_EINVAL, "pa_prefill: %d query heads not a multiple of %d KV heads", num_q_heads,
                 c.num_kv_heads);
+  if (!(scale > 0.0f) || !(scale < INFINITY))
+    return fail(PA_EINVAL, "pa_prefill: scale %g must be positive and finite", (double)scale);
   const int g = num_q_heads / c.num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(PA_EUNSUPPORTED, "pa_prefill: query heads per KV head = %d (built: 1, 2, 4, 8)", g);

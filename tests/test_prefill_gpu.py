@@ -115,6 +115,10 @@ def test_argument_errors(gpu_lib):
     with pytest.raises(gpu_lib.PagedKVError):  # 12 / 8 query heads
         gpu_lib.pa_prefill(to_dev(q)[:, :12].contiguous(), dc.k_cache, dc.v_cache, dc.block_tables,
                            dc.context_lens, to_dev(cu), 20, 20, 1.0)
+    for bad in (0.0, -0.1, float("inf"), float("nan")):  # the softmax scale must be positive and finite
+        with pytest.raises(gpu_lib.PagedKVError):
+            gpu_lib.pa_prefill(to_dev(q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, to_dev(cu), 20,
+                               20, bad)
 
 
 @pytest.mark.parametrize("name", ["prefill_llama3_8b", "prefill_chunked"])
