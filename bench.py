@@ -93,6 +93,12 @@ HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, per direction
 # admitted without the cache.
 PREFIX_WORKLOADS = {"prefix_cached_prompts": lambda: W.c8_prefix_cached_prompts()}
 PREFIX_METRIC = "prefix-cached prompt admission: prompt tokens/s (cached + computed)"
+# Shared-prefix copy-on-write: 256 sequences share a 2048-token prefix; each
+# of 8 steps copies 1% of the shared references, stores one token per
+# sequence and decodes.  GB/s of logical bytes (every sequence's whole
+# context) and of unique bytes (each distinct block's tokens once).
+COW_WORKLOADS = {"shared_prefix_cow": lambda: W.c4_shared_prefix()}
+COW_METRIC = "shared-prefix copy-on-write decode: logical GB/s (unique GB/s beside)"
 # KV waste of a serving loop (host simulation, no kernel): 4096 requests
 # through the KV slots one MI355X holds for Llama-3-8B, contiguous slabs
 # against the library's paged block manager (bs 16).
@@ -116,7 +122,7 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
                    choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(SWAP_WORKLOADS)
-                   + sorted(PREFIX_WORKLOADS) + sorted(WASTE_WORKLOADS))
+                   + sorted(PREFIX_WORKLOADS) + sorted(WASTE_WORKLOADS) + sorted(COW_WORKLOADS))
     p.add_argument("--partition", type=int, default=None,
                    help="decode partition_size (default: the workload's configuration)")
     p.add_argument("--cold-steps", type=int, default=10, help="cold-cache decode calls (0: skip)")
@@ -634,6 +640,159 @@ def prefix_main(args, torch, pkv, dev):
     return 0
 
 
+def cow_main(args, torch, pkv, dev):
+    """Shared-prefix steps: copy-on-write copies, then pa_decode_write (the
+    new tokens stored inside the balanced decode).  The host manager plans
+    every step before the timed region; the timed region replays the planned
+    steps in order (a replay copies the same blocks again and stores the same
+    tokens, so the pools stay as the plan left them)."""
+    log(f"workload {args.workload}: drawing inputs")
+    plan = COW_WORKLOADS[args.workload]()
+    bs, B, hkv, d = plan.block_size, plan.num_seqs, plan.num_kv_heads, plan.head_dim
+    prefix_blocks = plan.prefix_len // bs
+    block_bytes = hkv * bs * d * 2  # one pool's block, bf16
+
+    def dev_t(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    pool = pkv.BlockPool(plan.num_blocks, bs, plan.free_order)
+    kdev = torch.zeros((plan.num_blocks, hkv, bs, d), dtype=torch.bfloat16, device=dev)
+    vdev = torch.zeros_like(kdev)
+    pool.create(0, plan.prefix_len)
+    pkv.pa_write_kv(dev_t(plan.prefix_k.transpose(1, 0, 2)), dev_t(plan.prefix_v.transpose(1, 0, 2)),
+                    dev_t(np.asarray(pool.slots(0, 0, plan.prefix_len), np.int64)), kdev, vdev)
+    for s_ in range(1, B):
+        pool.fork(0, s_)
+    for s_ in range(B):
+        n = int(plan.suffix_lens[s_])
+        if n:
+            sl = np.array([pool.append(s_)[0] for _ in range(n)], np.int64)
+            pkv.pa_write_kv(dev_t(plan.suffix_k[s_].transpose(1, 0, 2)), dev_t(plan.suffix_v[s_].transpose(1, 0, 2)),
+                            dev_t(sl), kdev, vdev)
+
+    log(f"planning {plan.steps} steps with the host manager")
+    seqs = list(range(B))
+    steps, logical, unique, copies = [], [], [], []
+    host_s = 0.0
+    for step in range(plan.steps):
+        cands = [(s_, lb) for s_ in seqs for lb, blk in enumerate(pool.table(s_)[:prefix_blocks])
+                 if pool.refcount(int(blk)) > 1]
+        picks = plan.pick(cands)
+        t0 = time.perf_counter()  # the manager's calls only (the picks are the workload's)
+        pairs = [pool.cow(s_, lb) for s_, lb in picks]
+        pairs = np.array([pr for pr in pairs if pr is not None], np.int64).reshape(-1, 2)
+        slots, cow = pool.append_batch(seqs)
+        # copies an append asked for (none here: every tail block is private) go with the step's copies
+        pairs = np.concatenate([pairs, np.asarray(cow, np.int64).reshape(-1, 2)])
+        mb = max(len(pool.table(s_)) for s_ in seqs)
+        tables, lens = pool.tables(seqs, mb)
+        host_s += time.perf_counter() - t0
+        q = plan.step_q()
+        k_new, v_new = plan.step_tokens()
+        # bytes: logical = every sequence's context; unique = each distinct block's used tokens once
+        lens64 = lens.astype(np.int64)
+        tok_bytes = hkv * 2 * d * 2
+        logical.append(int(lens64.sum()) * tok_bytes + 4 * sum(W.ceil_div(int(c), bs) for c in lens64))
+        used = {}
+        for i, c in enumerate(lens64):
+            for j in range(W.ceil_div(int(c), bs)):
+                blk = int(tables[i, j])
+                used[blk] = max(used.get(blk, 0), min(bs, int(c) - j * bs))
+        unique.append(sum(used.values()) * tok_bytes)
+        copies.append(len(pairs))
+        steps.append((dev_t(pairs), dev_t(slots), dev_t(q), dev_t(k_new), dev_t(v_new), dev_t(tables), dev_t(lens),
+                      int(lens.max())))
+    max_ctx = max(st[-1] for st in steps)
+    out = torch.empty_like(steps[0][2])
+    ws_bytes = pkv.pa_decode_workspace_bytes(B, plan.num_q_heads, hkv, d, max_ctx, BALANCED)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) if ws_bytes else None
+    calls = []
+    for pairs, slots, q, k_new, v_new, tables, lens, mc in steps:
+        calls.append((pkv.prepare_copy_blocks(kdev, vdev, pairs),
+                      pkv.prepare_decode_write(k_new, v_new, slots, q, kdev, vdev, tables, lens, mc, plan.scale, out,
+                                               partition_size=BALANCED, workspace=ws)))
+    nplan = len(calls)
+    torch.cuda.synchronize()
+    for i in range(max(args.warmup, nplan)):
+        for c in calls[i % nplan]:
+            c()
+    torch.cuda.synchronize()
+    log(f"timed {args.steps} steps (replaying the {nplan} planned steps in order)")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for c in calls[i % nplan]:
+            c()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        calls[i % nplan][1]()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_s = e0.elapsed_time(e1) / 1e3 / args.steps
+    idx = [i % nplan for i in range(args.steps)]
+    write_bytes = B * hkv * d * 2 * 2 * 2  # new K and V rows read and stored
+    copy_bytes = [c * block_bytes * 2 * 2 for c in copies]  # K and V blocks read and written
+    step_logical = sum(logical[i] + write_bytes + copy_bytes[i] for i in idx) / args.steps
+    step_unique = sum(unique[i] + write_bytes + copy_bytes[i] for i in idx) / args.steps
+    dec_logical = sum(logical[i] + write_bytes for i in idx) / args.steps
+    dec_unique = sum(unique[i] + write_bytes for i in idx) / args.steps
+    step_s = wall / args.steps
+    result = {
+        "metric": COW_METRIC, "value": round(step_logical / step_s / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": max(args.warmup, nplan),
+        "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block placement)",
+        "config": {"workload": args.workload, "num_seqs": B, "prefix_tokens": plan.prefix_len,
+                   "num_q_heads": plan.num_q_heads, "num_kv_heads": hkv, "head_dim": d, "block_size": bs,
+                   "planned_steps": nplan, "cow_copies_per_step": int(np.mean(copies)),
+                   "pool_blocks": plan.num_blocks},
+        "unique_GBps": round(step_unique / step_s / 1e9, 1),
+        "logical_bytes_per_step": int(step_logical), "unique_bytes_per_step": int(step_unique),
+        "host_prep_us_per_step": round(host_s / nplan * 1e6, 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_unique / dec_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_unique / dec_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_gqa_balanced+merge_balanced_kernel", "avg_launch_us": round(dec_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(dec_unique),
+                     "logical_GBps": round(dec_logical / dec_s / 1e9, 1),
+                     "note": "achieved counts each distinct block's used tokens once (the bytes HBM must "
+                             "deliver at least); logical counts every sequence's whole context"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        from threadpoolctl import threadpool_info
+
+        from oracle import attention as A
+
+        kh = kdev.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh = vdev.view(torch.int16).cpu().numpy().view(np.uint16)
+        _, _, q0, _, _, t0d, l0d, _ = steps[-1]
+        qh = q0.view(torch.int16).cpu().numpy().view(np.uint16)
+        th, lh = t0d.cpu().numpy(), l0d.cpu().numpy()
+        done, n = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            s_ = n % B
+            A.decode(qh[s_:s_ + 1], kh, vh, th[s_:s_ + 1], lh[s_:s_ + 1], plan.scale, plan.dtype)
+            done += int(lh[s_]) * hkv * 2 * d * 2 + 4 * W.ceil_div(int(lh[s_]), bs)
+            n += 1
+        dt = time.perf_counter() - t0
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        result["cpu_baseline"] = {"value": round(done / dt / 1e9, 4), "unit": "GB/s (logical)", "cores": int(threads),
+                                  "kind": "oracle",
+                                  "sample": f"fp64 oracle, {n} sequence decodes of the last planned step, "
+                                            f"{dt:.1f} s wall", "seconds": round(dt, 2)}
+    pool.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def waste_main(args):
     """Host-only: the serving-loop simulation of both allocators, timed."""
     import paged_kv_cache_354_amd as pkv
@@ -723,6 +882,8 @@ def main(argv=None):
         return swap_main(args, torch, pkv, dev)
     if args.workload in PREFIX_WORKLOADS:
         return prefix_main(args, torch, pkv, dev)
+    if args.workload in COW_WORKLOADS:
+        return cow_main(args, torch, pkv, dev)
     make, default_part = WORKLOADS[args.workload]
     partition = default_part if args.partition is None else args.partition
 
@@ -827,6 +988,42 @@ def main(argv=None):
                 "decode_us_p90": round(float(np.percentile(cms, 90)) * 1e3, 2),
                 "decode_GBps": round(dec_bytes[0] / (float(np.median(cms)) / 1e3) / 1e9, 1),
                 "frac_of_peak": round(dec_bytes[0] / (float(np.median(cms)) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # Indirection overhead: the same decode (step 0's inputs, no store) on the
+    # shuffled pool and on a copy where every sequence's blocks sit at
+    # consecutive ids (identity placement), cold cache before each call.
+    indirection = None
+    if args.cold_steps > 0:
+        t0tab, l0 = plan.tables[0], plan.lens[0]
+        nbs = [W.ceil_div(int(c), case.block_size) for c in l0]
+        base = np.concatenate([[0], np.cumsum(nbs)]).astype(np.int64)
+        src = torch.from_numpy(np.concatenate([t0tab[i, :nbs[i]] for i in range(case.num_seqs)]).astype(np.int64))
+        src = src.to(dev)
+        idk, idv = k0.index_select(0, src), v0.index_select(0, src)
+        id_tab = np.full_like(t0tab, -1)
+        for i in range(case.num_seqs):
+            id_tab[i, :nbs[i]] = np.arange(base[i], base[i + 1])
+        variants = {
+            "shuffled": pkv.prepare_decode(q, k0, v0, tables[0], lens[0], max_ctx[0], case.scale, out,
+                                           partition_size=partition, workspace=ws),
+            "identity": pkv.prepare_decode(q, idk, idv, dev_t(id_tab), lens[0], max_ctx[0], case.scale, out,
+                                           partition_size=partition, workspace=ws),
+        }
+        med = {}
+        for name, call in variants.items():
+            n = args.cold_steps
+            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for i in range(n):
+                flush_sum = flush.sum()  # untimed cache eviction, as above
+                cev[i][0].record()
+                call()
+                cev[i][1].record()
+            torch.cuda.synchronize()
+            med[name] = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+        indirection = {"decode_us_shuffled": round(med["shuffled"], 2), "decode_us_identity": round(med["identity"], 2),
+                       "ratio_shuffled_over_identity": round(med["shuffled"] / med["identity"], 4),
+                       "note": "step 0 inputs, pa_decode without the store, cold cache, median of "
+                               f"{args.cold_steps} calls each"}
+        del idk, idv
     del flush
 
     traffic = measured_traffic(args.workload, partition)
@@ -870,6 +1067,7 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": int(np.mean(dec_bytes)),
         },
         "cold_cache": cold,
+        "indirection": indirection,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
