@@ -1008,21 +1008,21 @@ def main(argv=None):
             "identity": pkv.prepare_decode(q, idk, idv, dev_t(id_tab), lens[0], max_ctx[0], case.scale, out,
                                            partition_size=partition, workspace=ws),
         }
-        med = {}
-        for name, call in variants.items():
-            n = args.cold_steps
-            cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            for i in range(n):
+        n = 2 * args.cold_steps
+        cev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(n)] for name in variants}
+        for i in range(n):  # the two placements alternate, so drift hits both alike
+            for name, call in variants.items():
                 flush_sum = flush.sum()  # untimed cache eviction, as above
-                cev[i][0].record()
+                cev[name][i][0].record()
                 call()
-                cev[i][1].record()
-            torch.cuda.synchronize()
-            med[name] = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+                cev[name][i][1].record()
+        torch.cuda.synchronize()
+        med = {name: float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 for name, ev in cev.items()}
         indirection = {"decode_us_shuffled": round(med["shuffled"], 2), "decode_us_identity": round(med["identity"], 2),
                        "ratio_shuffled_over_identity": round(med["shuffled"] / med["identity"], 4),
                        "note": "step 0 inputs, pa_decode without the store, cold cache, median of "
-                               f"{args.cold_steps} calls each"}
+                               f"{n} alternating calls each"}
         del idk, idv
     del flush
 
