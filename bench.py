@@ -505,9 +505,10 @@ def prefix_cpu_baseline(plan, budget_s):
 def prefix_main(args, torch, pkv, dev):
     """Admission of a batch of prompts sharing a cached system prompt.
 
-    Host (planned before the timed region, timed on its own): for each
-    request the manager's create_cached, the slots of its uncached tokens
-    and the batch tables; the batch is released after the step (the system
+    Host (planned before the timed region, timed on its own): the batch
+    admission call (each request's cached prefix and the slots of its
+    uncached tokens) and the batch tables; the batch is released after the
+    step (the system
     prompt's blocks go back to the LRU list, where the next step finds
     them).  Device, per step: pa_write_kv of the uncached tokens, then
     pa_prefill of their queries over the whole prompts.  The same batch
@@ -541,9 +542,10 @@ def prefix_main(args, torch, pkv, dev):
     for t in range(nsteps):
         prompts = [plan.prompt(t, s) for s in range(B)]
         t0 = time.perf_counter()
-        cached = [pool.create_cached(s, prompts[s]) for s in range(B)]
-        slots = np.concatenate([np.asarray(pool.slots(s, cached[s], int(lens[s]) - cached[s]), np.int64)
-                                for s in range(B)])
+        cached, slots, refused = pool.create_cached_batch(list(range(B)), prompts)
+        if refused is not None:
+            raise RuntimeError(f"step {t}: admission refused: {refused}")
+        cached = cached.tolist()
         tables, ctx = pool.tables(list(range(B)), mb)
         for s in range(B):
             pool.release(s)

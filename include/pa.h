@@ -387,6 +387,20 @@ pa_status_t pa_pool_lru_list(const pa_pool *pool, int32_t *out, int32_t cap, int
  * do not fit (free + evictable blocks, not counting the hits themselves). */
 pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *tokens, int32_t num_tokens,
                                  int32_t *num_cached_tokens);
+/* pa_seq_create_cached for n requests in one call, in order: request i is
+ * sequence seqs[i] (host int64 [n]) with tokens[offsets[i] .. offsets[i+1])
+ * (host int32 tokens, host int64 offsets [n + 1], offsets[0] = 0).  For each
+ * admitted request num_cached[i] (host int32 [n]) receives its cached token
+ * count and slots (host int64, room for slots_cap >= offsets[n] entries)
+ * receives the slots of its uncached tokens, request after request, in
+ * position order: where pa_write_kv stores their K/V.  The first request that
+ * is refused ends the batch: the call returns its status (PA_ENOMEM when the
+ * pool is full), the requests before it stay admitted.  *num_admitted and
+ * *num_slots receive the admitted count and the slots written.  Argument
+ * errors (PA_EINVAL) admit nothing. */
+pa_status_t pa_seq_create_cached_batch(pa_pool *pool, const int64_t *seqs, int32_t n, const int32_t *tokens,
+                                       const int64_t *offsets, int32_t *num_cached, int64_t *slots,
+                                       int64_t slots_cap, int32_t *num_admitted, int64_t *num_slots);
 
 /* ------------------------------------------------------------------------
  * KV-cache waste of a serving loop (host only).

@@ -114,6 +114,7 @@ _SIGS = {
     "pa_pool_is_cached": (_i32, [_vp, _i32]),
     "pa_pool_lru_list": (_i32, [_vp, _P32, _i32, _P32]),
     "pa_seq_create_cached": (_i32, [_vp, _i64, _P32, _i32, _P32]),
+    "pa_seq_create_cached_batch": (_i32, [_vp, _P64, _i32, _P32, _P64, _P32, _P64, _i64, _P32, _P64]),
     "pa_waste_simulate": (_i32, [_i32, _i64, _i32, _P32, _P32, _P32, _i32, ctypes.POINTER(WasteStats)]),
 }
 
@@ -514,6 +515,40 @@ def pa_waste_simulate(mode, capacity, block_size, prompt_lens, output_lens, rese
     return st.as_dict()
 
 
+def pa_seq_create_cached_batch(pool, seqs, prompts):
+    """Admit ``prompts`` (sequences of token ids) as ``seqs`` in order until
+    one is refused.  Returns ``(num_cached, slots, refused)``: the cached
+    token count of each admitted request (int32 [k]), the slots of their
+    uncached tokens in order (int64), and None or the PoolExhausted /
+    PoolStateError that refused request k."""
+    seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
+    n = seqs.size
+    if len(prompts) != n:
+        raise PagedKVError(PA_EINVAL, "one prompt per sequence")
+    lens = np.array([len(p) for p in prompts], dtype=np.int64)
+    offsets = np.ascontiguousarray(np.concatenate([[0], np.cumsum(lens)]).astype(np.int64))
+    tokens = np.ascontiguousarray(np.concatenate([np.asarray(p, np.int32).reshape(-1) for p in prompts])
+                                  if n else np.zeros(0, np.int32))
+    cached = np.zeros(max(n, 1), dtype=np.int32)
+    slots = np.empty(max(int(offsets[-1]), 1), dtype=np.int64)
+    na, ns = ctypes.c_int32(), ctypes.c_int64()
+    st = load().pa_seq_create_cached_batch(
+        pool, _np_ptr(seqs, ctypes.c_int64) if n else None, n,
+        _np_ptr(tokens, ctypes.c_int32) if tokens.size else None, _np_ptr(offsets, ctypes.c_int64),
+        _np_ptr(cached, ctypes.c_int32), _np_ptr(slots, ctypes.c_int64), int(offsets[-1]), ctypes.byref(na),
+        ctypes.byref(ns))
+    refused = None
+    if st != PA_OK:
+        try:
+            _check(st)
+        except (PoolExhausted, PoolStateError) as e:
+            if st == PA_ESTATE or st == PA_ENOMEM:
+                refused = e
+            else:
+                raise
+    return cached[:na.value].copy(), slots[:ns.value].copy(), refused
+
+
 def pa_seq_create(pool, seq, num_tokens):
     _check(load().pa_seq_create(pool, seq, num_tokens))
 
@@ -673,6 +708,9 @@ class BlockPool:
 
     def create_cached(self, seq, tokens):
         return pa_seq_create_cached(self.handle, seq, tokens)
+
+    def create_cached_batch(self, seqs, prompts):
+        return pa_seq_create_cached_batch(self.handle, seqs, prompts)
 
     def num_cached(self):
         return pa_pool_num_cached(self.handle)

@@ -580,4 +580,42 @@ pa_status_t pa_seq_create_cached(pa_pool *pool, int64_t seq, const int32_t *toke
   return PA_OK;
 }
 
+pa_status_t pa_seq_create_cached_batch(pa_pool *pool, const int64_t *seqs, int32_t n, const int32_t *tokens,
+                                       const int64_t *offsets, int32_t *num_cached, int64_t *slots,
+                                       int64_t slots_cap, int32_t *num_admitted, int64_t *num_slots) {
+  if (!pool || n < 0 || !num_admitted || !num_slots || (n > 0 && (!seqs || !offsets || !num_cached)))
+    return fail(PA_EINVAL, "pa_seq_create_cached_batch: bad argument");
+  *num_admitted = 0;
+  *num_slots = 0;
+  if (n == 0) return PA_OK;
+  if (offsets[0] != 0) return fail(PA_EINVAL, "pa_seq_create_cached_batch: offsets[0] must be 0");
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t len = offsets[i + 1] - offsets[i];
+    if (len < 0 || len > INT32_MAX)
+      return fail(PA_EINVAL, "pa_seq_create_cached_batch: bad length %lld of request %d", (long long)len, i);
+  }
+  if (offsets[n] > 0 && (!tokens || !slots))
+    return fail(PA_EINVAL, "pa_seq_create_cached_batch: tokens or slots is NULL");
+  if (slots_cap < offsets[n])
+    return fail(PA_EINVAL, "pa_seq_create_cached_batch: slots has room for %lld, the batch has %lld tokens",
+                (long long)slots_cap, (long long)offsets[n]);
+  // Admit in order; the first request that is refused ends the batch.
+  int64_t out = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t len = (int32_t)(offsets[i + 1] - offsets[i]);
+    int32_t cached = 0;
+    if (pa_status_t st = pa_seq_create_cached(pool, seqs[i], tokens + offsets[i], len, &cached)) {
+      *num_slots = out;
+      return st;
+    }
+    const Seq &sq = pool->seqs.find(seqs[i])->second;
+    const int32_t bs = pool->block_size;
+    for (int64_t pos = cached; pos < len; ++pos) slots[out++] = (int64_t)sq.table[pos / bs] * bs + pos % bs;
+    num_cached[i] = cached;
+    *num_admitted = i + 1;
+  }
+  *num_slots = out;
+  return PA_OK;
+}
+
 }  // extern "C"

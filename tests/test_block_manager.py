@@ -293,3 +293,45 @@ def test_prefix_cache_hand_worked():
         assert not p.is_cached(5)
         if not is_model:
             p.close()
+
+
+def test_cached_batch_matches_one_by_one_admission():
+    """pa_seq_create_cached_batch == the model's create_cached applied to the
+    requests in order until one is refused (pool full or a sequence id in
+    use): the same cached counts, the same slots for the uncached tokens, the
+    same refusal and the same pool afterwards."""
+    rng = np.random.default_rng(31)
+    refusals = {"enomem": 0, "state": 0, None: 0}
+    for run in range(60):
+        nb = int(rng.integers(4, 40))
+        bs = int(rng.choice([1, 2, 4, 8]))
+        m, p = pair_of_pools(nb, bs, 0, run, cache=True)
+        live = []
+        for _ in range(int(rng.integers(1, 6))):  # batches, with releases in between
+            k = int(rng.integers(0, 6))
+            seqs = [int(x) for x in rng.integers(0, 12, k)]
+            prompts = [prompt(int(rng.integers(0, 4)), int(rng.integers(0, 40))) for _ in range(k)]
+            want_c, want_s, why = [], [], None
+            for s_, toks in zip(seqs, prompts):
+                try:
+                    c = m.create_cached(s_, toks)
+                except BM.PoolExhausted:
+                    why = "enomem"
+                    break
+                except BM.StateError:
+                    why = "state"
+                    break
+                want_c.append(c)
+                want_s += m.slots(s_, c, len(toks) - c)
+                live.append(s_)
+            got_c, got_s, refused = p.create_cached_batch(seqs, prompts)
+            got_why = None if refused is None else ("enomem" if isinstance(refused, pkv.PoolExhausted) else "state")
+            assert got_why == why
+            refusals[why] += 1
+            assert got_c.tolist() == want_c and got_s.tolist() == want_s
+            assert state_lib(p, list(m.tables), nb) == state_model(m)
+            for s_ in list(m.tables)[: int(rng.integers(0, len(m.tables) + 1))]:
+                m.release(s_)
+                p.release(s_)
+        p.close()
+    assert refusals["enomem"] > 5 and refusals["state"] > 5 and refusals[None] > 5
