@@ -111,3 +111,70 @@ def test_prefix_reuse_repeat_and_eviction(gpu_lib):
     pool.release(9)
     admit(4, a_tokens, 0)            # the prefix was evicted: computed again
     pool.close()
+
+
+def test_batched_admission_one_prefill_call(gpu_lib):
+    """Requests admitted together (pa_seq_create_cached_batch) with different
+    cached prefix lengths (none, one block, all full blocks, a repeat of a
+    whole prompt) are stored and prefilled in one pa_prefill call over all of
+    them; each request's rows equal the oracle's prefill of its whole prompt."""
+    pkv = gpu_lib
+    rng = np.random.default_rng(909)
+    nb = 64
+    pool = pkv.BlockPool(nb, BS, rng.permutation(nb))
+    pool.enable_prefix_cache()
+    kdev = torch.full((nb, HKV, BS, D), NAN_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vdev = torch.full_like(kdev.view(torch.int16), NAN_BF16).view(torch.bfloat16)
+    kv_of = {}
+
+    def kv_rows(tokens):
+        ks, vs = [], []
+        for pos, tok in enumerate(tokens):
+            key = (pos, int(tok))
+            if key not in kv_of:
+                kv_of[key] = (W.normal(rng, (HKV, D), W.BF16), W.normal(rng, (HKV, D), W.BF16))
+            ks.append(kv_of[key][0])
+            vs.append(kv_of[key][1])
+        return np.stack(ks), np.stack(vs)
+
+    sys_prompt = rng.integers(0, 1000, 50).astype(np.int32)  # 3 full blocks + 2 tokens
+    first = [np.concatenate([sys_prompt, rng.integers(2000, 3000, 9)]).astype(np.int32),
+             rng.integers(5000, 6000, 37).astype(np.int32)]
+
+    def admit(seqs, prompts, expect):
+        announce("prefix cache batch: admit", seqs)
+        cached, slots, refused = pool.create_cached_batch(seqs, prompts)
+        assert refused is None and cached.tolist() == expect
+        ks, vs, qs, cu, lens, refs = [], [], [], [0], [], []
+        for c, toks in zip(cached.tolist(), prompts):
+            k, v = kv_rows(toks)
+            ks.append(k[c:])
+            vs.append(v[c:])
+            q = W.normal(rng, (len(toks) - c, HQ, D), W.BF16)
+            qs.append(q)
+            cu.append(cu[-1] + len(toks) - c)
+            lens.append(len(toks))
+            kc, table = logical_pool(k)
+            vc, _ = logical_pool(v)
+            refs.append((P.prefill(q, kc, vc, table[None], np.array([len(toks)], np.int32),
+                                   np.array([0, len(toks) - c], np.int32), SCALE, W.BF16),
+                         float(np.max(np.abs(out_to_f64_np(vc))))))
+        assert slots.shape[0] == cu[-1]
+        pkv.pa_write_kv(to_dev(np.concatenate(ks)), to_dev(np.concatenate(vs)), to_dev(slots), kdev, vdev)
+        mb = max(W.ceil_div(n, BS) for n in lens)
+        tables, tl = pool.tables(seqs, mb)
+        assert tl.tolist() == lens
+        cu = np.array(cu, np.int32)
+        out = pkv.pa_prefill(to_dev(np.concatenate(qs)), kdev, vdev, to_dev(tables), to_dev(tl), to_dev(cu),
+                             int(np.max(np.diff(cu))), max(lens), SCALE, out_dtype=torch.float32)
+        got = out_to_f64(out)
+        for i, (ref, vmax) in enumerate(refs):
+            check_prefill(got[cu[i]:cu[i + 1]], ref, vmax, bf16_out=False)
+
+    admit([1, 2], first, [0, 0])
+    second = [np.concatenate([sys_prompt, rng.integers(7000, 8000, 20)]).astype(np.int32),  # 3 blocks cached
+              np.concatenate([sys_prompt[:16], rng.integers(9000, 9500, 30)]).astype(np.int32),  # 1 block
+              first[1].copy(),  # the whole prompt again: its 2 full blocks cached
+              rng.integers(10000, 11000, 5).astype(np.int32)]  # nothing cached
+    admit([3, 4, 5, 6], second, [48, 16, 32, 0])
+    pool.close()
