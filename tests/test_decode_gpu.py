@@ -220,6 +220,60 @@ def test_balanced_workspace_reuse_garbage_and_repeats(gpu_lib):
                     assert torch.equal(got, first[key]), (c.name, rep)
 
 
+def test_balanced_under_graph_replay(gpu_lib):
+    """The balanced split (decode kernel + merge kernel) captured in a HIP
+    graph and replayed, on a batch whose shares cut most sequences (16
+    sequences of U{1500..2500} tokens, 32/8 heads), with a workspace filled
+    with random bytes first.  Eager calls on the same workspace run between
+    replays.  Every replay and every eager call is bitwise equal to the first
+    eager result, which matches the fp64 oracle."""
+    rng = np.random.default_rng(81)
+    lens = rng.integers(1500, 2500, size=16, endpoint=True)
+    case = W.make_case("graph_replay", seed=82, dtype=W.BF16, context_lens=lens, num_q_heads=32,
+                       num_kv_heads=8, head_dim=128, block_size=16, poison=True)
+    dc = DevCase(case)
+    dc.write(gpu_lib)
+    kc, vc = oracle_after_write(case)
+    ref = A.decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
+    need = gpu_lib.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                             case.head_dim, case.max_context, BAL)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    out = torch.empty((case.num_seqs, case.num_q_heads, case.head_dim), dtype=torch.float32, device="cuda")
+
+    def call():
+        gpu_lib.pa_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.max_context,
+                          case.scale, partition_size=BAL, workspace=ws, out=out, out_dtype=torch.float32)
+
+    announce(case.name, "eager")
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    check_decode(out_to_f64(eager), ref, False)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        announce(case.name, "replay", rep)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), ("replay", rep)
+        if rep % 2:
+            out.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), ("eager between replays", rep)
+
+
 def test_argument_errors(gpu_lib):
     announce("argument errors")
     case = small_bf16_case(51, num_seqs=2)
