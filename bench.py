@@ -118,8 +118,12 @@ def log(*a):
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--plan-steps", type=int, default=20,
+                   help="decode workloads: distinct planned steps (lengths grow by one per step), replayed "
+                        "cyclically by the warmup and the timed steps")
+    p.add_argument("--warmup", type=int, default=200,
+                   help="untimed steps first (200 bring the GPU to the steady state of a serving loop)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD,
                    choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(SWAP_WORKLOADS)
                    + sorted(PREFIX_WORKLOADS) + sorted(WASTE_WORKLOADS) + sorted(COW_WORKLOADS))
@@ -891,7 +895,12 @@ def main(argv=None):
 
     log(f"workload {args.workload}: drawing inputs")
     case = make()
-    nplan = max(args.steps, args.warmup, 1)
+    # Warmup and timed steps replay the planned steps cyclically: a replayed
+    # step stores the same tokens in the same slots and attends over the same
+    # contexts, all of its work done again, so the contexts the timed steps
+    # see stay within the workload's distribution (+ at most plan_steps - 1
+    # tokens) however many steps are timed.
+    nplan = max(1, min(args.steps, args.plan_steps))
     plan = StepPlan(case, nplan, pkv)
     log(f"planned {nplan} steps, host prep {plan.host_prep_us:.1f} us/step, pool {case.num_blocks} blocks")
 
@@ -949,7 +958,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        for call in steps[i]:
+        for call in steps[i % nplan]:
             call()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -961,15 +970,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.steps):
-        steps[i][2]()
+        steps[i % nplan][2]()
     e1.record()
     torch.cuda.synchronize()
     dec_avg_s = e0.elapsed_time(e1) / 1e3 / args.steps
 
-    totals = [plan.step_bytes(i, case) for i in range(args.steps)]
+    totals = [plan.step_bytes(i % nplan, case) for i in range(args.steps)]
     step_bytes = sum(sum(t) for t in totals)
     dec_bytes = [t[0] + (t[1] if fused else 0) for t in totals]  # what the timed decode call moves
-    tokens = sum(int(plan.lens[i].astype(np.int64).sum()) for i in range(args.steps))
+    tokens = sum(int(plan.lens[i % nplan].astype(np.int64).sum()) for i in range(args.steps))
     ms_per_step = wall / args.steps * 1e3
     value = step_bytes / wall / 1e9
     achieved = float(np.mean(dec_bytes)) / dec_avg_s / 1e9
@@ -1050,7 +1059,7 @@ def main(argv=None):
             "context_len_mean": round(float(plan.lens[0].mean()), 1),
             "context_len_max": int(plan.lens[0].max()),
             "partition_size": partition, "seed": case.meta.get("seed"),
-            "kv_pool_copies": len(layers), "write_fused_into_decode": fused,
+            "kv_pool_copies": len(layers), "write_fused_into_decode": fused, "planned_steps": nplan,
         },
         "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(tokens / wall, 1),
