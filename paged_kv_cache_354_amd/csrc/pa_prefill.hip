@@ -229,19 +229,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     }
   };
   auto store_tile = [&](int b, int kt0) {
-    const bool full = kt0 + kKeys <= kend;  // uniform
+    if (kt0 + kKeys <= kend) {  // uniform: a full tile, stored as loaded
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
-      const int item = tid + u * kThreads;
-      if (item >= ITEMS) break;  // uniform per wave
-      const int ch = item % C;
-      const int kp = item / C;
+      for (int u = 0; u < NCH; ++u) {
+        const int item = tid + u * kThreads;
+        if (item >= ITEMS) break;  // uniform per wave
+        const int ch = item % C;
+        const int kp = item / C;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint4 kv = kreg[u][e], vv = vreg[u][e];
-        if (!full && kt0 + 2 * kp + e >= kend) kv = vv = make_uint4(0, 0, 0, 0);
-        sh.k[b][2 * kp + e][ch] = kv;
-        sh.v[b][2 * kp + e][ch] = vv;
+        for (int e = 0; e < 2; ++e) {
+          sh.k[b][2 * kp + e][ch] = kreg[u][e];
+          sh.v[b][2 * kp + e][ch] = vreg[u][e];
+        }
+      }
+    } else {
+      // the last, partial tile: keys at or past kend are stored as zeros (a
+      // real branch, so that full tiles do not pay for the selects)
+      asm volatile("");
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int item = tid + u * kThreads;
+        if (item >= ITEMS) break;  // uniform per wave
+        const int ch = item % C;
+        const int kp = item / C;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bool past = kt0 + 2 * kp + e >= kend;
+          sh.k[b][2 * kp + e][ch] = past ? make_uint4(0, 0, 0, 0) : kreg[u][e];
+          sh.v[b][2 * kp + e][ch] = past ? make_uint4(0, 0, 0, 0) : vreg[u][e];
+        }
       }
     }
   };
@@ -306,17 +322,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
         // raw scores; the scale (positive) enters through the max and the
         // exponent's fma
         float z[8];
-        float mx = -INFINITY;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int key = kt0 + 16 * hh + 4 * g + e;
-            float v = st[rb][hh][e];
-            if (diag) v = key <= prow[rb] ? v : -INFINITY;
-            z[4 * hh + e] = v;
-            mx = fmaxf(mx, v);
-          }
+          for (int e = 0; e < 4; ++e) z[4 * hh + e] = st[rb][hh][e];
+        if (diag) {
+          // A real branch: most tiles lie wholly below the block's first row,
+          // and the compiler would otherwise turn the mask into selects that
+          // every tile pays for (an empty volatile asm cannot be speculated).
+          asm volatile("");
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kt0 + 16 * hh + 4 * g + e > prow[rb]) z[4 * hh + e] = -INFINITY;
+        }
+        float mx = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
         mx *= a.qscale;
         // The reference max m moves only when some score passes it by more
         // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
