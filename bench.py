@@ -1035,6 +1035,27 @@ def main(argv=None):
                        "note": "step 0 inputs, pa_decode without the store, cold cache, median of "
                                f"{n} alternating calls each"}
         del idk, idv
+
+    # Practical read ceiling of this device: pa_read_probe streams the 1 GiB
+    # flush buffer (4x the Infinity Cache) with coalesced non-temporal loads,
+    # back to back on the launch stream, timed with HIP events.
+    read_ceiling = None
+    if args.cold_steps > 0:
+        sink = torch.empty(pkv.PA_READ_PROBE_WORKGROUPS, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            pkv.pa_read_probe(flush, sink)
+        n = 20
+        e0.record()
+        for _ in range(n):
+            pkv.pa_read_probe(flush, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        probe_s = e0.elapsed_time(e1) / 1e3 / n
+        ceiling = FLUSH_BYTES / probe_s / 1e9
+        read_ceiling = {"GBps": round(ceiling, 1), "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4),
+                        "bytes": FLUSH_BYTES, "kernel": "read_probe_kernel",
+                        "decode_frac_of_ceiling": round(achieved / ceiling, 4),
+                        "note": "plain streaming read (pa_read_probe), mean of 20 back-to-back calls"}
     del flush
 
     traffic = measured_traffic(args.workload, partition)
@@ -1079,6 +1100,7 @@ def main(argv=None):
         },
         "cold_cache": cold,
         "indirection": indirection,
+        "read_ceiling": read_ceiling,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -445,6 +445,25 @@ pa_status_t pa_waste_simulate(int32_t mode, int64_t capacity, int32_t block_size
                               const int32_t *output_lens, const int32_t *reserve_lens, int32_t num_requests,
                               pa_waste_stats *out);
 
+/* ---------------------------------------------------------------------------
+ * pa_read_probe -- measurement helper, not a step of the attention path.
+ * Streams a device buffer once with 16-byte non-temporal loads, each of
+ * PA_READ_PROBE_WORKGROUPS workgroups walking one contiguous run of it; its
+ * rate is the practical read ceiling of the device, reported beside the HBM
+ * peak when the decode's bandwidth is measured.
+ *
+ *   buf     device, 16-byte aligned, `bytes` long (a multiple of 16; 0 is
+ *           allowed); read only.
+ *   sink    device uint32 [PA_READ_PROBE_WORKGROUPS]: workgroup w writes the
+ *           XOR of the 32-bit words it read, so the XOR of all of sink is
+ *           the XOR of every 32-bit word of buf (a check that every byte was
+ *           read).
+ * Caller-owned memory; asynchronous on `stream`; PA_EINVAL for a size that
+ * is not a multiple of 16, a misaligned buffer or a NULL pointer.
+ * ------------------------------------------------------------------------ */
+#define PA_READ_PROBE_WORKGROUPS 8192
+pa_status_t pa_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

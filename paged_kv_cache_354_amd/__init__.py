@@ -116,6 +116,7 @@ _SIGS = {
     "pa_seq_create_cached": (_i32, [_vp, _i64, _P32, _i32, _P32]),
     "pa_seq_create_cached_batch": (_i32, [_vp, _P64, _i32, _P32, _P64, _P32, _P64, _i64, _P32, _P64]),
     "pa_waste_simulate": (_i32, [_i32, _i64, _i32, _P32, _P32, _P32, _i32, ctypes.POINTER(WasteStats)]),
+    "pa_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
 }
 
 EXPORTED = tuple(_SIGS)
@@ -222,6 +223,28 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     _check(load().pa_copy_blocks(kp, vp, ctypes.byref(desc),
                                  _dev(src_dst_pairs, "src_dst_pairs", torch.int64, (n, 2)), n,
                                  _stream(stream)))
+
+
+PA_READ_PROBE_WORKGROUPS = 8192
+
+
+def pa_read_probe(buf, sink=None, stream=None):
+    """Stream the contiguous device tensor ``buf`` once (a measurement helper:
+    the practical read ceiling); returns the uint32 ``sink`` of
+    ``PA_READ_PROBE_WORKGROUPS`` words whose XOR is the XOR of every 32-bit
+    word of ``buf``."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(PA_READ_PROBE_WORKGROUPS, dtype=torch.int32, device=buf.device)
+    if (not sink.is_cuda or sink.dtype not in (torch.int32, torch.uint32) or not sink.is_contiguous()
+            or sink.numel() < PA_READ_PROBE_WORKGROUPS):
+        raise ValueError(f"sink must be a contiguous int32 GPU tensor of >= {PA_READ_PROBE_WORKGROUPS} words")
+    _check(load().pa_read_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                _stream(stream)))
+    return sink
 
 
 def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, stream=None):
