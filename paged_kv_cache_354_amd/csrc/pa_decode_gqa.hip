@@ -47,9 +47,11 @@
 // output.  K and V rows are streamed with non-temporal loads.  Each K load
 // covers half of a 128-byte line of 16 rows; the line's other half is read
 // by the next load, issued right after it, and still comes from L2 (the
-// measured HBM bytes stay within 2% of the algorithmic ones).  Marking K
+// measured HBM bytes stay within 3% of the algorithmic ones).  Marking K
 // non-temporal as well took ~1 us off a 100 us call on the Llama-3-8B-shaped
 // batch (MI355X, median of 185 dispatches).
+
+#include <atomic>
 
 #include "pa_decode_common.h"
 
@@ -674,12 +676,15 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) 
 // Launch limits of one balanced-kernel instance on the current device: the
 // workgroups that fit on it at once for a given dynamic LDS size, and the
 // dynamic LDS a workgroup may take.  Queried once per (instance, device, LDS
-// size) and kept.
+// size) and kept, each device's entry in one atomic word (callers on several
+// threads see either no entry or a whole one).
 template <int D, int G, bool BIG>
 struct BalancedLimits {
   static int resident(int dev, size_t dyn_lds) {
-    static int cache[64][2] = {};  // [device] -> {dyn_lds + 1, workgroups}
-    if (cache[dev][0] == (int)dyn_lds + 1) return cache[dev][1];
+    static std::atomic<uint64_t> cache[64];  // [device] -> (dyn_lds + 1) << 32 | workgroups
+    const uint64_t key = (uint64_t)(dyn_lds + 1) << 32;
+    const uint64_t hit = cache[dev].load(std::memory_order_relaxed);
+    if ((hit & ~0xffffffffull) == key) return (int)(hit & 0xffffffffull);
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_gqa_balanced<D, G, BIG>, kThreads,
                                                      dyn_lds) != hipSuccess ||
@@ -687,21 +692,22 @@ struct BalancedLimits {
       return kBalancedMaxWorkgroups;
     int n = per_cu * cus;
     n = n < 1 ? 1 : (n > kBalancedMaxWorkgroups ? kBalancedMaxWorkgroups : n);
-    cache[dev][0] = (int)dyn_lds + 1;
-    cache[dev][1] = n;
+    cache[dev].store(key | (uint32_t)n, std::memory_order_relaxed);
     return n;
   }
   static size_t max_dyn_lds(int dev) {
-    static size_t cache[64] = {};
-    if (cache[dev]) return cache[dev];
+    static std::atomic<size_t> cache[64];
+    const size_t hit = cache[dev].load(std::memory_order_relaxed);
+    if (hit) return hit;
     int max_lds = 0;
     hipFuncAttributes fa{};
     if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
         hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(decode_gqa_balanced<D, G, BIG>)) !=
             hipSuccess)
       return 64 * 1024 - 36 * 1024;  // the 64 KiB floor minus the largest static share
-    cache[dev] = max_lds > (int)fa.sharedSizeBytes ? (size_t)max_lds - fa.sharedSizeBytes : 1;
-    return cache[dev];
+    const size_t v = max_lds > (int)fa.sharedSizeBytes ? (size_t)max_lds - fa.sharedSizeBytes : 1;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
   }
 };
 

@@ -274,6 +274,50 @@ def test_balanced_under_graph_replay(gpu_lib):
             assert torch.equal(out, eager), ("eager between replays", rep)
 
 
+def test_balanced_concurrent_callers(gpu_lib):
+    """Two host threads call the balanced decode at once, each on its own
+    stream, with batches of different sizes (different dynamic LDS, so the
+    library's per-device launch-limit entry alternates between them); every
+    call's output is bitwise the single-threaded one."""
+    import threading
+
+    cases = [small_bf16_case(91, num_seqs=12), small_bf16_case(92, num_seqs=300, hi=200)]
+    dcs = [DevCase(c) for c in cases]
+    refs = [dc.decode(gpu_lib, partition_size=BAL, out_dtype=torch.float32) for dc in dcs]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            c, dc = cases[i], dcs[i]
+            stream = torch.cuda.Stream()
+            ws = torch.empty(gpu_lib.pa_decode_workspace_bytes(c.num_seqs, c.num_q_heads, c.num_kv_heads,
+                                                               c.head_dim, c.max_context, BAL),
+                             dtype=torch.uint8, device="cuda")
+            outs = []
+            with torch.cuda.stream(stream):
+                for _ in range(40):
+                    outs.append(gpu_lib.pa_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                                                  dc.context_lens, c.max_context, c.scale, partition_size=BAL,
+                                                  workspace=ws, out_dtype=torch.float32, stream=stream))
+            stream.synchronize()
+            for o in outs:
+                if not torch.equal(o, refs[i]):
+                    errors.append(f"case {i}: output differs")
+                    break
+        except Exception as e:  # reported below
+            errors.append(f"case {i}: {e!r}")
+
+    announce("concurrent balanced callers")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a caller did not finish"
+    assert not errors, errors
+
+
 def test_argument_errors(gpu_lib):
     announce("argument errors")
     case = small_bf16_case(51, num_seqs=2)
