@@ -70,7 +70,8 @@ def out_to_f64_np(a):
 
 
 @pytest.mark.parametrize("hq,hkv,d,bs", [(32, 8, 128, 16), (64, 8, 128, 16), (16, 8, 128, 32),
-                                         (8, 8, 128, 16), (16, 4, 64, 8), (32, 8, 64, 1)])
+                                         (8, 8, 128, 16), (16, 4, 64, 8), (32, 8, 64, 1), (16, 8, 64, 16),
+                                         (64, 8, 64, 32)])
 def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
     rng = np.random.default_rng(hq + d + bs)
     lens = [1, 15, 16, 17, 100, 333, 64, 40]
