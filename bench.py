@@ -196,6 +196,8 @@ def decode_kernels(case, partition, fused=False):
     gqa = case.dtype == W.BF16 and case.num_q_heads // case.num_kv_heads in (4, 8) and case.head_dim in (64, 128, 256)
     if gqa and partition == -1:
         return "decode_gqa_balanced+merge_balanced_kernel"
+    if partition == -1:  # the vector-ALU kernel: 1024-token partitions past 1024 tokens
+        partition = 1024 if case.max_context > 1024 else 0
     pre = "write_kv_kernel+" if fused else ""
     if gqa:
         return pre + "decode_gqa_kernel" + ("+merge_kernel" if partition else "")

@@ -171,10 +171,12 @@ pa_status_t pa_swap_blocks(const void *src_k, const void *src_v, const pa_cache_
  *                   workgroup slot of the GPU, and merges the sequences a
  *                   share boundary cuts.  Used for bf16 pools with 4 or 8 query
  *                   heads per KV head, up to 8192 sequences and
- *                   num_seqs * (max_context_len + 271) < 2^31; other
- *                   configurations run unpartitioned, or in 4096-token
- *                   partitions when a context is longer than that (vector-ALU
- *                   kernel: longer than one workgroup's table).  The result
+ *                   num_seqs * (max_context_len + 271) < 2^31.  Other
+ *                   bf16 batches with 4 or 8 query heads per KV head run in
+ *                   4096-token partitions when a context is longer than
+ *                   that; fp32 pools and 1 or 2 query heads per KV head run
+ *                   in 1024-token partitions when a context is longer than
+ *                   that; anything shorter runs unpartitioned.  The result
  *                   is the same from call to call for the same inputs.
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes, 256-byte aligned, when partition_size != 0 (may be

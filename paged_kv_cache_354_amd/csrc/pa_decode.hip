@@ -424,11 +424,18 @@ int64_t parts_for(int64_t max_ctx, int64_t part) {
   return np < 1 ? 1 : np;
 }
 
-// Partition size used when the balanced split is asked for but cannot run:
-// the vector-ALU kernel with a context beyond one workgroup's table, or a
-// batch whose prefix sums would not fit (a multiple of every supported block
-// size).
+// Partition size used when the balanced split is asked for but a grouped-
+// query batch's prefix sums would not fit (a multiple of every supported
+// block size).
 constexpr int kValuBalancedFallbackP = 4096;
+// Partition size of the vector-ALU kernel (fp32 pools, 1 or 2 query heads
+// per KV head) under PA_PARTITION_BALANCED when a context is longer than
+// that: the long sequences of a skewed batch are cut into pieces that spread
+// over the GPU instead of leaving a tail of lone long workgroups (measured
+// on MI355X, 256 MHA sequences of lognormal lengths up to 8192: 873 us per
+// call unpartitioned, 820 / 810 / 821 us with 512 / 1024 / 2048-token
+// partitions).  Also within one workgroup's table at every block size.
+constexpr int kValuBalancedP = 1024;
 
 bool uses_gqa_kernel(int dtype, int group, int head_dim) {
   return dtype == PA_BF16 && pa::gqa_mfma_supported(group, head_dim);
@@ -446,10 +453,10 @@ extern "C" size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_head
   if (partition_size > 0)
     return partitioned_layout(num_seqs, num_q_heads, head_dim, parts_for(mc, partition_size)).total;
   if (partition_size == PA_PARTITION_BALANCED) {
-    // whichever kernel runs: the balanced split, or the vector-ALU fallback
+    // whichever kernel runs: the balanced split, or partitions (the vector-ALU
+    // kernel's are the finer, so their layout covers the other fallback's)
     const size_t bal = balanced_layout(num_seqs, num_q_heads, num_kv_heads, head_dim).total;
-    const size_t fb =
-        partitioned_layout(num_seqs, num_q_heads, head_dim, parts_for(mc, kValuBalancedFallbackP)).total;
+    const size_t fb = partitioned_layout(num_seqs, num_q_heads, head_dim, parts_for(mc, kValuBalancedP)).total;
     return bal > fb ? bal : fb;
   }
   return 0;
@@ -542,9 +549,12 @@ pa_status_t decode_call(const void *q, int32_t num_seqs, int32_t num_q_heads, co
                       (int64_t)num_seqs * ((((int64_t)ctx_cap + 15) & ~(int64_t)15) + 256) <= 0x7fffffff;
     if (gqa && fits) {
       mode = pa::kModeBalanced;
-    } else if (gqa ? ctx_cap > kValuBalancedFallbackP : ctx_blocks > kMaxTableLds) {
+    } else if (gqa && ctx_cap > kValuBalancedFallbackP) {
       mode = pa::kModePartitioned;
       part = kValuBalancedFallbackP;
+    } else if (!gqa && ctx_cap > kValuBalancedP) {
+      mode = pa::kModePartitioned;
+      part = kValuBalancedP;
     }
   }
   if (!gqa && mode == pa::kModePartitioned && part / c.block_size > kMaxTableLds)
