@@ -23,8 +23,9 @@
 //   - balanced: a grid of one resident workgroup per slot of the GPU, each
 //     taking an equal share of all (KV head, sequence, token) work in that
 //     order (lengths rounded up to 16, plus a fixed cost per sequence), so
-//     no tail of lone long workgroups is left.  A workgroup that holds a whole sequence writes its output
-//     directly; sequences cut between workgroups are combined by
+//     no tail of lone long workgroups is left; the shares of one XCD are
+//     contiguous.  A workgroup that holds a whole sequence writes its
+//     output directly; sequences cut between workgroups are combined by
 //     merge_balanced_kernel.
 //
 // Lane layouts (lane l, 64 per wave):
