@@ -67,6 +67,31 @@ def test_shape_grid(gpu_lib, dtype, hq, hkv, d, bs):
     run_and_check(gpu_lib, case, sorted(set(parts)) + [BAL])
 
 
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs", [(W.F32, 4, 4, 64, 16), (W.BF16, 8, 8, 128, 16),
+                                               (W.BF16, 8, 4, 128, 32), (W.F32, 4, 2, 128, 8)])
+def test_balanced_vector_kernel_partitions_long_contexts(gpu_lib, dtype, hq, hkv, d, bs):
+    """Under the balanced mode the vector-ALU kernel (fp32 pools, 1 or 2 query
+    heads per KV head) cuts contexts longer than 1024 tokens into 1024-token
+    partitions and merges them; lengths on both sides of the cut and at its
+    multiples, poisoned tails, against the fp64 oracle, through a workspace
+    filled with random bytes first."""
+    lens = [1, 1023, 1024, 1025, 2048, 2049, 3000, 17]
+    case = W.make_case(f"valu_bal_{dtype}_{hq}_{hkv}_{d}_{bs}", seed=hq * 31 + d + bs, dtype=dtype,
+                       context_lens=lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                       poison=True)
+    dc = DevCase(case)
+    dc.write(gpu_lib)
+    kc, vc = oracle_after_write(case)
+    ref = A.decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale, case.dtype)
+    need = gpu_lib.pa_decode_workspace_bytes(case.num_seqs, hq, hkv, d, case.max_context, BAL)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    for od in ([None] if dtype == W.F32 else [None, torch.float32]):
+        announce(case.name, "BAL", "out", od)
+        got = gpu_lib.pa_decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, case.max_context,
+                                case.scale, partition_size=BAL, workspace=ws, out_dtype=od)
+        check_decode(out_to_f64(got), ref, dtype == W.BF16 and od is None)
+
+
 def test_poisoned_tails_unused_blocks_and_write_slot(gpu_lib):
     case = small_bf16_case(7, poison=True)
     run_and_check(gpu_lib, case, [0, 16, 128, BAL])
