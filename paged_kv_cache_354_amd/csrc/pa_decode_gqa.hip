@@ -53,6 +53,7 @@
 // batch (MI355X, median of 185 dispatches).
 
 #include <atomic>
+#include <type_traits>
 
 #include "pa_decode_common.h"
 
@@ -628,10 +629,13 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) 
   if (w1 == w2) return;  // one workgroup held the whole sequence and wrote it
   const size_t pair = (size_t)kvh * B + s;
   // A thread owns E of the G * D outputs (elements tid + k kThreads).  The
-  // loads of up to 4 pieces for all E elements are issued together, then
-  // folded into running (max, sum, acc) in piece order: the latency is one
-  // round trip per 4 pieces, whatever E is.
-  constexpr int kBatch = 4;
+  // loads of kBatch pieces for all E elements are issued together, then
+  // folded into running (max, sum, acc) in piece order: one round trip per
+  // kBatch pieces, whatever E is.  kBatch is 16 when a sequence has more than
+  // 8 pieces, else 4 (loads of 16 for a sequence of few pieces cost more than
+  // the round trips they save; measured on MI355X, 8 x 32k tokens, ~12
+  // pieces each: 177.9 -> 175.7 us per call).  The fold order, and so the
+  // result, is the same for both.
   constexpr int E = (G * D + kThreads - 1) / kThreads;
   float M[E], L[E], A[E];
 #pragma unroll
@@ -640,33 +644,41 @@ __global__ __launch_bounds__(kThreads) void merge_balanced_kernel(DecodeArgs a) 
     L[k] = 0.0f;
     A[k] = 0.0f;
   }
-  for (int64_t w0 = w1; w0 <= w2; w0 += kBatch) {
-    float pm[kBatch][E], pl_[kBatch][E], po[kBatch][E];
+  auto fold_all = [&](auto batch_tag) {
+    constexpr int kBatch = decltype(batch_tag)::value;
+    for (int64_t w0 = w1; w0 <= w2; w0 += kBatch) {
+      float pm[kBatch][E], pl_[kBatch][E], po[kBatch][E];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t w = w0 + u <= w2 ? w0 + u : w2;  // repeats are masked below
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t w = w0 + u <= w2 ? w0 + u : w2;  // repeats are masked below
 #pragma unroll
-      for (int k = 0; k < E; ++k) {
-        const int idx = min((int)threadIdx.x + k * kThreads, G * D - 1);  // past the end: unused
-        const size_t slot = (w + pair) * G + idx / D;
-        pm[u][k] = a.part_m[slot];
-        pl_[u][k] = a.part_l[slot];
-        po[u][k] = a.part_o[slot * D + idx % D];
+        for (int k = 0; k < E; ++k) {
+          const int idx = min((int)threadIdx.x + k * kThreads, G * D - 1);  // past the end: unused
+          const size_t slot = (w + pair) * G + idx / D;
+          pm[u][k] = a.part_m[slot];
+          pl_[u][k] = a.part_l[slot];
+          po[u][k] = a.part_o[slot * D + idx % D];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (w0 + u <= w2) {
+#pragma unroll
+          for (int k = 0; k < E; ++k) {
+            const float mn = fmaxf(M[k], pm[u][k]);
+            const float f0 = exp2_fast(M[k] - mn), f1 = exp2_fast(pm[u][k] - mn);
+            L[k] = L[k] * f0 + pl_[u][k] * f1;
+            A[k] = A[k] * f0 + po[u][k] * f1;
+            M[k] = mn;
+          }
+        }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (w0 + u > w2) break;
-#pragma unroll
-      for (int k = 0; k < E; ++k) {
-        const float mn = fmaxf(M[k], pm[u][k]);
-        const float f0 = exp2_fast(M[k] - mn), f1 = exp2_fast(pm[u][k] - mn);
-        L[k] = L[k] * f0 + pl_[u][k] * f1;
-        A[k] = A[k] * f0 + po[u][k] * f1;
-        M[k] = mn;
-      }
-    }
-  }
+  };
+  if (w2 - w1 >= 8)
+    fold_all(std::integral_constant<int, 16>{});
+  else
+    fold_all(std::integral_constant<int, 4>{});
 #pragma unroll
   for (int k = 0; k < E; ++k) {
     const int idx = threadIdx.x + k * kThreads;
