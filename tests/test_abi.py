@@ -55,3 +55,13 @@ def test_workspace_bytes_host_only():
     want = up((64 + b + 1) * 4) + 2 * up(slots * 4 * 4) + up(slots * 4 * d * 4)
     assert pkv.pa_decode_workspace_bytes(b, hq, hkv, d, 4096, pkv.PA_PARTITION_BALANCED) == want
     assert pkv.pa_decode_workspace_bytes(b, hq, 5, d, 4096, 0) == 0  # 32 / 5 heads: invalid
+    # balanced with one query head per KV head (vector-ALU kernel): 1024-token
+    # partitions past 1024 tokens, whose layout outgrows the balanced one
+    b, hq, hkv, d, mc = 256, 40, 40, 128, 8192
+    np_ = mc // 1024
+    ml = up(b * hq * np_ * 4)
+    part = 2 * ml + up(b * hq * np_ * d * 4)
+    slots = 2048 + b * hkv
+    bal = up((64 + b + 1) * 4) + 2 * up(slots * 1 * 4) + up(slots * 1 * d * 4)
+    assert part > bal
+    assert pkv.pa_decode_workspace_bytes(b, hq, hkv, d, mc, pkv.PA_PARTITION_BALANCED) == part
