@@ -60,6 +60,7 @@ constexpr int kThreads = 256;  // 4 wave64s
 constexpr int kKeys = 32;      // keys per tile
 constexpr int kRB = 2;         // 16-row blocks per wave
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
+constexpr int kRankSeqs = 32; // batches up to this many sequences run longest first
 constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
 constexpr int kWaitVmem = 0x0F70;
@@ -108,25 +109,61 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared<D> sh;
 
   // Work order: query block (last first: causal blocks near the end see the
-  // most keys), sequence, head group, KV head; contiguous ranges per XCD.
-  // With the KV head slowest, XCD x takes the same KV head(s) of every
-  // sequence: the XCDs get equal shares however unequal the sequences are,
-  // and an XCD's L2 holds the keys and values of its own heads only.
+  // most keys), sequence (longest context first), head group, KV head;
+  // contiguous ranges per XCD.  With the KV head slowest, XCD x takes the
+  // same KV head(s) of every sequence: the XCDs get equal shares however
+  // unequal the sequences are, and an XCD's L2 holds the keys and values of
+  // its own heads only.  Longest first within an XCD keeps a long
+  // sequence's workgroups from starting last and running alone at the end.
   const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
   int r = xcd_work_id(blockIdx.x, n_work);
   const int qb = a.q_blocks - 1 - r % a.q_blocks;
   r /= a.q_blocks;
-  const int s = r % a.num_seqs;
+  const int rank = r % a.num_seqs;
   r /= a.num_seqs;
   const int hg = r % HG;
   const int kvh = r / HG;
-
-  const int lo = a.cu_seqlens[s];
-  const int n = a.cu_seqlens[s + 1] - lo;
+  int s = rank, lo, n, ctx;
+  if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
+    // the sequence of this rank by context length, longest first, ties by
+    // index (a permutation, so exactly one sequence has it).  The lengths
+    // and the query offsets are staged together, so the choice costs no
+    // extra round trip; sh.tbl is scratch here (the block ids are staged
+    // into it below).
+    __shared__ int chosen;
+    int32_t *len = sh.tbl;
+    int32_t *cu = sh.tbl + kRankSeqs;
+    for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
+      cu[i] = a.cu_seqlens[i];
+      if (i < a.num_seqs) {
+        const int c = a.context_lens[i];
+        len[i] = c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
+      }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.num_seqs; t += kThreads) {
+      const int lt = len[t];
+      int rk = 0;
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const int lj = len[j];
+        rk += lj > lt || (lj == lt && j < t);
+      }
+      if (rk == rank) chosen = t;
+    }
+    __syncthreads();
+    s = chosen;
+    lo = cu[s];
+    n = cu[s + 1] - lo;
+    ctx = len[s];
+    __syncthreads();  // every thread has read the scratch before it is overwritten
+  } else {
+    lo = a.cu_seqlens[s];
+    n = a.cu_seqlens[s + 1] - lo;
+    ctx = a.context_lens[s];
+    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  }
   const int q0 = qb * TQ;
   if (q0 >= n) return;
-  int ctx = a.context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
   const int first_pos = ctx - n;  // position of query 0 of the sequence
 
   const int tid = threadIdx.x;

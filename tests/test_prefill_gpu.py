@@ -12,7 +12,8 @@ with max|V| over the values the sequence attends to, and 1e-4 for fp32
 accumulation order and exp2 (the decode kernels' fp32 bar).
 
 Cases cover whole prompts, chunks after a cached context, one query per
-sequence, empty chunks and chunks longer than the context (zero rows), on
+sequence, empty chunks and chunks longer than the context (zero rows),
+batches on both sides of the longest-first ordering's size limit, on
 pools poisoned with NaN wherever no visible key lives.
 """
 
@@ -77,6 +78,17 @@ def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
     lens = [1, 15, 16, 17, 100, 333, 64, 40]
     nq = [1, 15, 16, 17, 100, 50, 1, 0]  # whole prompts, a chunk after cached keys, decode-like, empty
     case, q, cu = make_prefill(int(rng.integers(1 << 20)), lens, nq, hq, hkv, d, bs)
+    run_case(gpu_lib, case, q, cu)
+
+
+@pytest.mark.parametrize("nseq", [1, 32, 33])
+def test_length_ordered_work_with_ties(gpu_lib, nseq):
+    # batches of 2..32 sequences are taken longest context first (ties by
+    # index), larger ones in index order; repeated lengths make ties
+    rng = np.random.default_rng(71 + nseq)
+    lens = [int(x) for x in rng.choice([16, 48, 48, 130, 1], size=nseq)]
+    nq = [int(min(l, x)) for l, x in zip(lens, rng.integers(0, 40, size=nseq))]
+    case, q, cu = make_prefill(int(rng.integers(1 << 20)), lens, nq, 32, 8, 128, 16)
     run_case(gpu_lib, case, q, cu)
 
 
