@@ -256,7 +256,8 @@ pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_ma
  *   out           device [num_tokens][num_q_heads][head_dim] of out_dtype
  *                 (PA_F32 or PA_BF16).
  * Built for bf16 pools, head_dim 64 or 128, 1, 2, 4 or 8 query heads per KV
- * head and power-of-two block sizes up to 256; otherwise PA_EUNSUPPORTED.
+ * head, power-of-two block sizes up to 256 and num_kv_heads x block_size
+ * below 2^31 (rows per pool block); otherwise PA_EUNSUPPORTED.
  * Scores and the softmax are fp32; the probabilities enter the product with
  * V rounded to bf16.  num_seqs, num_tokens or max_query_len == 0: no-op.
  * ------------------------------------------------------------------------ */

@@ -171,6 +171,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int nl = lane & 15;
+  // byte addresses of the lanes 16 and 32 away (the 4 lanes of a row)
+  const int xor16 = (lane ^ 16) << 2;
+  const int xor32 = (lane ^ 32) << 2;
   const int h = kvh * G + hg * GW + wave % GW;
   const int tok0 = q0 + (wave / GW) * 16 * kRB;  // the wave's first query
   // keys the workgroup needs, and the ones this wave needs
@@ -206,7 +209,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   }
 
   const int32_t *trow = a.block_tables + (size_t)s * a.max_blocks;
-  const size_t block_rows = (size_t)a.num_kv_heads * a.block_size;
+  // rows per block; the host keeps it below 2^31, and block ids are
+  // clamped into the pool (non-negative), so one 32 x 32 -> 64-bit multiply
+  // places a block
+  const uint32_t block_rows = (uint32_t)(a.num_kv_heads * a.block_size);
   const size_t head_rows = (size_t)kvh * a.block_size;
 
   // The block ids of keys [0, kend), staged once when they fit.
@@ -237,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
     int blk;
     if constexpr (STAGED) blk = sh.tbl[kk >> a.log2_bs];
     else blk = max(0, min(trow[kk >> a.log2_bs], a.num_blocks - 1));
-    return (size_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
+    return (uint64_t)(uint32_t)blk * block_rows + head_rows + (kk & (a.block_size - 1));
   };
   // A tile below kend needs neither the clamp nor the zero fill; the two
   // keys of a pair share a block (and sit in consecutive rows) unless the
@@ -361,15 +367,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
           // and the compiler would otherwise turn the mask into selects that
           // every tile pays for (an empty volatile asm cannot be speculated).
           asm volatile("");
+          // key kt0 + 16hh + 4g + e lies past the row when 16hh + e > lim
+          const int lim = prow[rb] - kt0 - 4 * g;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (kt0 + 16 * hh + 4 * g + e > prow[rb]) z[4 * hh + e] = -INFINITY;
+              if (16 * hh + e > lim) z[4 * hh + e] = -INFINITY;
         }
+        // maximum (NaN-propagating) takes matrix-core results as they are;
+        // fmaxf would first quiet each of them, one more instruction each
         float mx = z[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+        for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
         mx *= a.qscale;
         // The reference max m moves only when some score passes it by more
         // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
@@ -378,8 +388,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
         // max over its 4 lanes, so the 4 lanes of a row keep one m.  The
         // result does not depend on m.
         if (__any(mx > m[rb] + kLazyMax)) {
-          mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
+          mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
           const float mn = fmaxf(m[rb], mx);
           const float alpha = exp2_fast(m[rb] - mn);
           m[rb] = mn;
@@ -388,13 +398,12 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
           for (int j = 0; j < OB; ++j) o[rb][j] *= alpha;
         }
         f32x8_t p;
-        float ps = 0.0f;
         const float negm = -m[rb];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2_fast(fmaf(z[e], a.qscale, negm));
-          ps += p[e];
-        }
+        for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], a.qscale, negm));
+        float ps = p[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) ps += p[e];
         l[rb] += ps;
         pb[rb] = __builtin_convertvector(p, bf16x8_t);
       }
@@ -489,6 +498,9 @@ extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num
     return fail(PA_EUNSUPPORTED, "pa_prefill: head_dim %d (built: 64, 128)", c.head_dim);
   if (c.block_size > 256 || (c.block_size & (c.block_size - 1)))
     return fail(PA_EUNSUPPORTED, "pa_prefill: block_size %d (powers of two up to 256)", c.block_size);
+  if ((int64_t)c.num_kv_heads * c.block_size > INT32_MAX)
+    return fail(PA_EUNSUPPORTED, "pa_prefill: %d KV heads x block size %d: over 2^31 rows per block", c.num_kv_heads,
+                c.block_size);
   if (num_q_heads % c.num_kv_heads)
     return fail(PA_EINVAL, "pa_prefill: %d query heads not a multiple of %d KV heads", num_q_heads,
                 c.num_kv_heads);

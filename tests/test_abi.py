@@ -65,3 +65,15 @@ def test_workspace_bytes_host_only():
     bal = up((64 + b + 1) * 4) + 2 * up(slots * 1 * 4) + up(slots * 1 * d * 4)
     assert part > bal
     assert pkv.pa_decode_workspace_bytes(b, hq, hkv, d, mc, pkv.PA_PARTITION_BALANCED) == part
+
+
+def test_prefill_rejects_blocks_over_2_31_rows_before_any_device_call():
+    # 2^24 KV heads x 256-token blocks: the kernel places a block with one
+    # 32 x 32-bit multiply, so the host refuses such a pool up front (the
+    # check precedes every pointer use, so NULLs are fine here)
+    lib = pkv.load()
+    cache = pkv.PaCache(num_blocks=1, block_size=256, num_kv_heads=1 << 24, head_dim=128, dtype=pkv.PA_BF16)
+    st = lib.pa_prefill(None, 1, 1 << 24, None, 1, 1, None, None, ctypes.byref(cache), None, 1, None, 1, 1.0,
+                        None, pkv.PA_F32, None)
+    assert st == pkv.PA_EUNSUPPORTED
+    assert "rows per block" in lib.pa_last_error().decode()
