@@ -92,6 +92,16 @@ def test_balanced_vector_kernel_partitions_long_contexts(gpu_lib, dtype, hq, hkv
         check_decode(out_to_f64(got), ref, dtype == W.BF16 and od is None)
 
 
+@pytest.mark.parametrize("hq,hkv,parts", [(8, 2, [0, 4096, BAL]), (4, 4, [2048, BAL])])
+def test_tables_past_4096_blocks(gpu_lib, hq, hkv, parts):
+    # 1-token blocks: a sequence of more than 4096 blocks outgrows the block
+    # ids one workgroup stages in LDS; the matrix-core kernel stages them in
+    # sub-ranges one after another, the vector kernel runs partitioned
+    case = W.make_case(f"bs1_long_{hq}_{hkv}", seed=59, dtype=W.BF16, context_lens=[9000, 4097, 1, 300],
+                       num_q_heads=hq, num_kv_heads=hkv, head_dim=128, block_size=1)
+    run_and_check(gpu_lib, case, parts)
+
+
 def test_poisoned_tails_unused_blocks_and_write_slot(gpu_lib):
     case = small_bf16_case(7, poison=True)
     run_and_check(gpu_lib, case, [0, 16, 128, BAL])

@@ -105,6 +105,13 @@ def test_long_prompts_many_tiles(gpu_lib):
     run_case(gpu_lib, case, q, cu)
 
 
+def test_table_read_from_hbm_past_2048_blocks(gpu_lib):
+    # 1-token blocks: a workgroup that needs more than 2048 block ids reads
+    # them from the table in HBM instead of staging them in LDS
+    case, q, cu = make_prefill(47, [2100, 3000, 2049], [33, 64, 1], 32, 8, 128, 1)
+    run_case(gpu_lib, case, q, cu)
+
+
 def test_placement_permutation_is_bitwise_invariant(gpu_lib):
     case, q, cu = make_prefill(51, [300, 129], [300, 65], 32, 8, 128, 16, poison=False)
     perm = np.random.default_rng(5).permutation(case.num_blocks)
