@@ -870,7 +870,7 @@ def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
+        print(f"bench.py: runs on exactly one GPU (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the decode path has no multi-GPU mode", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
