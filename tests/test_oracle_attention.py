@@ -16,7 +16,7 @@ import torch
 
 import workloads as W
 from oracle import attention as A
-from oracle.numerics import to_f64
+from widen import torch_to_f64 as to_f64
 
 
 def scatter_case(rng, lens, hq, hkv, d, bs, dtype=W.F32, num_blocks=None, scale=None):

@@ -17,7 +17,7 @@ import torch
 import workloads as W
 from oracle import attention as A
 from oracle import prefill as P
-from oracle.numerics import to_f64
+from widen import torch_to_f64 as to_f64
 
 
 def scatter_prefill(rng, lens, nq, hq, hkv, d, bs, dtype=W.BF16, scale=None):
