@@ -106,6 +106,8 @@ WASTE_WORKLOADS = {"waste_llama3_8b_c2": lambda: W.waste_case("waste_llama3_8b_c
                    "waste_llama3_8b_c5": lambda: W.waste_case("waste_llama3_8b_c5")}
 WASTE_METRIC = "KV-cache waste: % of held KV slots holding no token (paged blocks; contiguous slabs beside)"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+DECODE_TIMED_CALLS = 200   # back-to-back decode calls in the roofline's event bracket (at least --steps)
+DECODE_PER_CALL = 100      # decode calls timed one by one for the per-call distribution
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_{}_traffic.md")
 DECODE_SRCS = [os.path.join(ROOT, "paged_kv_cache_354_amd", "csrc", f)
                for f in ("pa_decode.hip", "pa_decode_gqa.hip", "pa_decode_common.h")]
@@ -234,34 +236,98 @@ def measured_traffic(workload, partition):
 
 # --- CPU baseline (oracle) -------------------------------------------------------------
 
-def cpu_baseline(case, plan, budget_s):
-    """fp64 oracle on the step-0 batch, sequence by sequence, until the time
-    budget is spent; rate scaled to the metric's unit."""
-    from threadpoolctl import threadpool_info
+def oracle_cores():
+    """Cores the oracle baseline may use: this process's CPU affinity, at
+    most 16 (one GPU's share of a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _oracle_decode_worker(job):
+    """One oracle worker (a fresh process, one BLAS thread): decodes its
+    sequences of the batch one after another, cycling, for ``budget``
+    seconds; returns (bytes, tokens, sequence decodes, seconds)."""
+    (shm_k, shm_v, pool_shape, pool_dtype, q, tables, lens, seqs, scale, dtype, budget, hkv, d, elt, bs) = job
+    from multiprocessing import shared_memory
+
+    from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
 
+    mk, mv = shared_memory.SharedMemory(name=shm_k), shared_memory.SharedMemory(name=shm_v)
+    try:
+        k = np.ndarray(pool_shape, dtype=pool_dtype, buffer=mk.buf)
+        v = np.ndarray(pool_shape, dtype=pool_dtype, buffer=mv.buf)
+        done, tok, n = 0, 0, 0
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            while True:
+                s = seqs[n % len(seqs)]
+                A.decode(q[s:s + 1], k, v, tables[s:s + 1], lens[s:s + 1], scale, dtype)
+                c = int(lens[s])
+                done += c * hkv * 2 * d * elt + 4 * W.ceil_div(c, bs)
+                tok += c
+                n += 1
+                if time.perf_counter() - t0 >= budget:
+                    break
+            dt = time.perf_counter() - t0
+        del k, v
+    finally:
+        mk.close()
+        mv.close()
+    return done, tok, n, dt
+
+
+def cpu_baseline(case, plan, budget_s, workers=None):
+    """The fp64 oracle on the step-0 batch on this host's cores: the
+    sequences are dealt round-robin to ``oracle_cores()`` worker processes
+    (spawned fresh, one BLAS thread each, the pools in shared memory), each
+    decoding its sequences one by one, cycling, for the time budget; the rate
+    is scaled to the metric's unit.  A single worker alone is timed after
+    that (a quarter of the budget) for the one-core figure."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
     tables, lens = plan.tables[0], plan.lens[0]
-    elt = case.elt_bytes()
-    done_bytes, done_tok, n = 0, 0, 0
-    t0 = time.perf_counter()
-    while True:  # cycle over the batch until the budget is spent
-        s = n % case.num_seqs
-        A.decode(case.q[s:s + 1], case.k_cache, case.v_cache, tables[s:s + 1], lens[s:s + 1], case.scale,
-                 case.dtype)
-        c = int(lens[s])
-        done_bytes += c * case.num_kv_heads * 2 * case.head_dim * elt + 4 * W.ceil_div(c, case.block_size)
-        done_tok += c
-        n += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"fp64 oracle, {n} sequence decodes cycling over the {case.num_seqs} sequences "
-                      f"of step 0 ({done_tok} tokens x {case.num_q_heads} q heads), {dt:.1f} s wall",
-            "tokens_per_s": round(done_tok / dt, 1), "seconds": round(dt, 2)}
+    n_work = workers or oracle_cores()
+    shms = []
+    try:
+        for arr in (case.k_cache, case.v_cache):
+            m = shared_memory.SharedMemory(create=True, size=arr.nbytes)
+            np.ndarray(arr.shape, arr.dtype, buffer=m.buf)[...] = arr
+            shms.append(m)
+
+        def jobs(n, budget):
+            return [(shms[0].name, shms[1].name, case.k_cache.shape, case.k_cache.dtype, case.q, tables, lens,
+                     list(range(w, case.num_seqs, n)), case.scale, case.dtype, budget, case.num_kv_heads,
+                     case.head_dim, case.elt_bytes(), case.block_size) for w in range(n)]
+
+        ctx = mp.get_context("spawn")
+        t0 = time.perf_counter()
+        with ctx.Pool(n_work) as pool:
+            res = pool.map(_oracle_decode_worker, jobs(n_work, budget_s))
+        wall = time.perf_counter() - t0
+        with ctx.Pool(1) as pool:
+            one = pool.map(_oracle_decode_worker, jobs(1, budget_s / 4))[0]
+    finally:
+        for m in shms:
+            m.close()
+            m.unlink()
+    done = sum(r[0] for r in res)
+    tok = sum(r[1] for r in res)
+    n = sum(r[2] for r in res)
+    dt = max(r[3] for r in res)
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": n_work, "kind": "oracle",
+            "sample": f"fp64 oracle, {n_work} worker processes x 1 BLAS thread, the {case.num_seqs} sequences "
+                      f"of step 0 dealt round-robin, {n} sequence decodes ({tok} tokens x {case.num_q_heads} "
+                      f"q heads) in {dt:.1f} s per worker ({wall:.1f} s with process start)",
+            "tokens_per_s": round(tok / dt, 1), "seconds": round(dt, 2),
+            "single_core": {"value": round(one[0] / one[3] / 1e9, 4), "unit": "GB/s",
+                            "tokens_per_s": round(one[1] / one[3], 1), "seconds": round(one[3], 2),
+                            "sequence_decodes": one[2]}}
 
 
 def causal_flops(context_lens, cu_seqlens, num_q_heads, head_dim):
@@ -285,7 +351,8 @@ def prefill_flops(pc):
 def prefill_cpu_baseline(pc, budget_s):
     """fp64 oracle rows (every head of a token) cycling over the chunk's
     tokens until the budget is spent; TFLOP/s on the same flop count."""
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
+    one_core = threadpool_limits(1)  # the oracle on one BLAS thread
 
     from oracle import prefill as P
 
@@ -306,7 +373,8 @@ def prefill_cpu_baseline(pc, budget_s):
         flops += max(pos + 1, 0) * c.num_q_heads * 4 * c.head_dim
         n += 1
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads = 1  # run under threadpool_limits(1): one core
+    one_core.restore_original_limits()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 oracle rows (all {c.num_q_heads} heads of a token), {n} tokens drawn at random "
                       f"from the chunk, {dt:.1f} s wall", "seconds": round(dt, 2)}
@@ -467,7 +535,8 @@ def prefix_cpu_baseline(plan, budget_s):
     random, attending over the request's whole prompt (the cached path's
     work); prompt tokens/s = computed rows/s x prompt tokens per computed
     token."""
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
+    one_core = threadpool_limits(1)  # the oracle on one BLAS thread
 
     from oracle import prefill as P
 
@@ -505,7 +574,8 @@ def prefix_cpu_baseline(plan, budget_s):
     dt = time.perf_counter() - t0
     prompt_tokens = plan.num_seqs * plan.prefix_len + int(plan.suffix_lens.sum())
     per_computed = prompt_tokens / int(plan.suffix_lens.sum())
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads = 1  # run under threadpool_limits(1): one core
+    one_core.restore_original_limits()
     return {"value": round(rows_done / dt * per_computed, 3), "unit": "prompt tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 oracle rows (all {plan.num_q_heads} heads of a token) for {rows_done} suffix queries "
@@ -779,7 +849,8 @@ def cow_main(args, torch, pkv, dev):
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_limits
+        one_core = threadpool_limits(1)  # the oracle on one BLAS thread
 
         from oracle import attention as A
 
@@ -796,7 +867,8 @@ def cow_main(args, torch, pkv, dev):
             done += int(lh[s_]) * hkv * 2 * d * 2 + 4 * W.ceil_div(int(lh[s_]), bs)
             n += 1
         dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        threads = 1  # run under threadpool_limits(1): one core
+        one_core.restore_original_limits()
         result["cpu_baseline"] = {"value": round(done / dt / 1e9, 4), "unit": "GB/s (logical)", "cores": int(threads),
                                   "kind": "oracle",
                                   "sample": f"fp64 oracle, {n} sequence decodes of the last planned step, "
@@ -844,7 +916,8 @@ def waste_main(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_limits
+        one_core = threadpool_limits(1)  # the oracle on one BLAS thread
 
         from oracle import waste as WS
 
@@ -854,7 +927,8 @@ def waste_main(args):
         st = WS.simulate("paged", small.capacity, small.block_size, small.prompt_lens, small.output_lens,
                          small.reserve_lens)
         dt = time.perf_counter() - t0
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        threads = 1  # run under threadpool_limits(1): one core
+        one_core.restore_original_limits()
         result["cpu_baseline"] = {
             "value": round(100.0 * st.waste(), 3), "unit": "%", "cores": int(threads), "kind": "oracle",
             "sample": f"the oracle's paged run on 1/{k} of the requests and of the pool "
@@ -955,41 +1029,12 @@ def main(argv=None):
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    log(f"warmup {args.warmup}")
-    for i in range(args.warmup):
-        for call in steps[i % nplan]:
-            call()
-    torch.cuda.synchronize()
+    totals = [plan.step_bytes(i % nplan, case) for i in range(max(args.steps, nplan))]
+    dec_bytes = [t[0] + (t[1] if fused else 0) for t in totals]  # what one decode call moves
 
-    log(f"timed {args.steps} steps, partition_size {partition}")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        for call in steps[i % nplan]:
-            call()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # Decode launches alone, back to back, same per-step inputs: HIP events on
-    # the launch stream around the run give the average launch duration
-    # (an event between launches would add its own gap on the GPU).
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(args.steps):
-        steps[i % nplan][2]()
-    e1.record()
-    torch.cuda.synchronize()
-    dec_avg_s = e0.elapsed_time(e1) / 1e3 / args.steps
-
-    totals = [plan.step_bytes(i % nplan, case) for i in range(args.steps)]
-    step_bytes = sum(sum(t) for t in totals)
-    dec_bytes = [t[0] + (t[1] if fused else 0) for t in totals]  # what the timed decode call moves
-    tokens = sum(int(plan.lens[i % nplan].astype(np.int64).sum()) for i in range(args.steps))
-    ms_per_step = wall / args.steps * 1e3
-    value = step_bytes / wall / 1e9
-    achieved = float(np.mean(dec_bytes)) / dec_avg_s / 1e9
-
+    # The cache-flushed, placement and read-ceiling measurements run first:
+    # they are reported beside the timed steps, and they also take the GPU out
+    # of its idle state before the warmup steps, as a serving loop would be.
     cold = None
     if args.cold_steps > 0:
         n = args.cold_steps
@@ -1046,7 +1091,8 @@ def main(argv=None):
     # Practical read ceiling of this device: pa_read_probe streams the 1 GiB
     # flush buffer (4x the Infinity Cache) with coalesced non-temporal loads,
     # back to back on the launch stream, timed with HIP events.
-    read_ceiling = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe_s = None
     if args.cold_steps > 0:
         sink = torch.empty(pkv.PA_READ_PROBE_WORKGROUPS, dtype=torch.int32, device=dev)
         for _ in range(3):
@@ -1058,12 +1104,61 @@ def main(argv=None):
         e1.record()
         torch.cuda.synchronize()
         probe_s = e0.elapsed_time(e1) / 1e3 / n
+    del flush
+
+    log(f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        for call in steps[i % nplan]:
+            call()
+    torch.cuda.synchronize()
+
+    log(f"timed {args.steps} steps, partition_size {partition}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for call in steps[i % nplan]:
+            call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Decode calls alone, back to back, over the same per-step inputs, timed
+    # with HIP events on the launch stream.  One call is queued before the
+    # first event, so the bracket opens on a busy queue and holds no launch
+    # latency of its own; no event sits between the calls (an event between
+    # launches adds its own gap on the GPU).
+    n_dec = max(args.steps, DECODE_TIMED_CALLS)
+    steps[nplan - 1][2]()
+    e0.record()
+    for i in range(n_dec):
+        steps[i % nplan][2]()
+    e1.record()
+    torch.cuda.synchronize()
+    dec_avg_s = e0.elapsed_time(e1) / 1e3 / n_dec
+    # and each call on its own between two events (a distribution; each
+    # bracket also holds the event's own gap, so it reads a little high)
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(DECODE_PER_CALL)]
+    steps[nplan - 1][2]()
+    for i in range(DECODE_PER_CALL):
+        pev[i][0].record()
+        steps[i % nplan][2]()
+        pev[i][1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in pev]) * 1e3  # us
+
+    step_bytes = sum(sum(totals[i % nplan]) for i in range(args.steps))
+    tokens = sum(int(plan.lens[i % nplan].astype(np.int64).sum()) for i in range(args.steps))
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / wall / 1e9
+    dec_mean_bytes = float(np.mean([dec_bytes[i % nplan] for i in range(n_dec)]))
+    achieved = dec_mean_bytes / dec_avg_s / 1e9
+    read_ceiling = None
+    if probe_s is not None:
         ceiling = FLUSH_BYTES / probe_s / 1e9
         read_ceiling = {"GBps": round(ceiling, 1), "frac_of_peak": round(ceiling / HBM_PEAK_GBS, 4),
                         "bytes": FLUSH_BYTES, "kernel": "read_probe_kernel",
                         "decode_frac_of_ceiling": round(achieved / ceiling, 4),
                         "note": "plain streaming read (pa_read_probe), mean of 20 back-to-back calls"}
-    del flush
 
     traffic = measured_traffic(args.workload, partition)
     result = {
@@ -1103,8 +1198,14 @@ def main(argv=None):
             "traffic": traffic,
             "kernel": decode_kernels(case, partition, fused),
             "avg_launch_us": round(dec_avg_s * 1e6, 2),
-            "algorithmic_bytes_per_launch": int(np.mean(dec_bytes)),
+            "algorithmic_bytes_per_launch": int(dec_mean_bytes),
+            "timed_calls": n_dec,
         },
+        "decode_per_call_us": {"median": round(float(np.median(per_call)), 2),
+                               "p10": round(float(np.percentile(per_call, 10)), 2),
+                               "p90": round(float(np.percentile(per_call, 90)), 2),
+                               "calls": DECODE_PER_CALL,
+                               "note": "each call between its own two HIP events, warm, rotating pools"},
         "cold_cache": cold,
         "indirection": indirection,
         "read_ceiling": read_ceiling,

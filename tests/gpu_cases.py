@@ -90,3 +90,37 @@ def small_bf16_case(seed, num_seqs=6, lo=1, hi=700, extra=(1, 15, 16, 17), **kw)
     return W.make_case(f"small_bf16_s{seed}", seed=seed + 1, dtype=W.BF16, context_lens=lens,
                        num_q_heads=kw.pop("num_q_heads", 32), num_kv_heads=kw.pop("num_kv_heads", 8),
                        head_dim=kw.pop("head_dim", 128), block_size=kw.pop("block_size", 16), **kw)
+
+
+def oracle_decode_all(case, k_cache, v_cache, block_tables=None, context_lens=None, q=None, workers=16):
+    """The fp64 oracle over every (sequence, query head) of a batch, the
+    sequences split over threads (the oracle's NumPy work releases the GIL);
+    each thread runs ``oracle.attention.decode`` on its own slice."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import attention as A
+
+    q = case.q if q is None else q
+    bt = case.block_tables if block_tables is None else block_tables
+    cl = case.context_lens if context_lens is None else context_lens
+    b = q.shape[0]
+    cuts = np.linspace(0, b, min(workers, max(b, 1)) + 1).astype(int)
+
+    def run(i):
+        lo, hi = cuts[i], cuts[i + 1]
+        return A.decode(q[lo:hi], k_cache, v_cache, bt[lo:hi], cl[lo:hi], case.scale, case.dtype)
+
+    with ThreadPoolExecutor(len(cuts) - 1) as ex:
+        parts = list(ex.map(run, range(len(cuts) - 1)))
+    return np.concatenate(parts, axis=0) if parts else np.zeros(q.shape, np.float64)
+
+
+def check_bf16_is_rounded_f32(got_bf16_dev, got_f32_dev):
+    """The bf16 output is the fp32 output rounded to nearest even, element by
+    element (the kernels compute in fp32 in the same order for either output
+    type and round once at the store)."""
+    bits = to_host(got_bf16_dev)
+    f32 = to_host(got_f32_dev)
+    expect = W.round_to_bf16(f32)
+    bad = bits != expect
+    assert not bad.any(), f"{int(bad.sum())} bf16 outputs are not the rounded fp32 outputs"

@@ -112,26 +112,3 @@ def test_fused_no_sequences_still_stores(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(dc.k_cache.view(torch.int16), ref.k_cache.view(torch.int16))
     assert torch.equal(dc.v_cache.view(torch.int16), ref.v_cache.view(torch.int16))
-
-
-@pytest.mark.parametrize("name", ["llama3_8b_b64", "long_ctx_32k"])
-def test_fused_full_size(gpu_lib, name):
-    """The benchmarked launch (balanced split, fused store) at full size:
-    pools and output bitwise those of the two calls, and sampled rows against
-    the oracle."""
-    case = W.c2_llama8b_b64() if name == "llama3_8b_b64" else W.c3_long_context()
-    announce("decode_write full", name)
-    res = both_ways(gpu_lib, case, BAL, torch.float32)
-    assert_same(res)
-    got = res[1][2].cpu().numpy().astype(np.float64)
-    del res
-    torch.cuda.empty_cache()
-    kc, vc = oracle_after_write(case)
-    grp = case.num_q_heads // case.num_kv_heads
-    rng = np.random.default_rng(11)
-    rows = {(int(s), int(h)) for s, h in zip(rng.integers(0, case.num_seqs, 24),
-                                             rng.integers(0, case.num_q_heads, 24))}
-    for s, h in sorted(rows):
-        ref = A.decode_one(case.q[s, h], kc, vc, case.block_tables[s], case.context_lens[s], case.scale,
-                           case.dtype, h // grp)
-        check_decode(got[s, h], ref, bf16_out=False)
