@@ -231,6 +231,35 @@ pa_status_t pa_decode_write(const void *k, const void *v, const int64_t *slot_ma
                             int32_t out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_decode_write_noalloc -- pa_decode_write without a workspace argument,
+ * for callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, result and errors: those of pa_decode_write, minus workspace
+ * and workspace_bytes; the same kernels run.  The scratch those kernels need
+ * (partial softmax statistics of the cut sequences, the split's header) is a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES inside the library: each
+ * GPU the library runs on holds its own copy until the process ends.  A call
+ * whose scratch need (pa_decode_workspace_bytes of the same arguments)
+ * exceeds it returns PA_EINVAL and enqueues nothing.  The call allocates and
+ * frees nothing (no hipMalloc / hipFree, no allocating library routine);
+ * the first call on a device looks up that device's scratch address once.
+ * The scratch starts each call in whatever state the last one left; the
+ * kernels write every byte they read before reading it.  Calls that overlap
+ * on one GPU (other streams, other threads) share that scratch and race:
+ * serialise them.
+ * ------------------------------------------------------------------------ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+pa_status_t pa_decode_write_noalloc(const void *k, const void *v, const int64_t *slot_mapping,
+                                    int32_t num_tokens, const void *q, int32_t num_seqs,
+                                    int32_t num_q_heads, void *k_cache, void *v_cache,
+                                    const pa_cache_t *cache, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                    int32_t max_context_len, float scale, int32_t partition_size,
+                                    void *out, int32_t out_dtype, void *stream);
+
+/* ---------------------------------------------------------------------------
  * pa_prefill -- causal attention of a chunk of new queries per sequence (a
  * prompt, or its next piece), reading keys and values through the block table.
  * (foundry PagedAttention page, Concept and How it works: a sequence's keys

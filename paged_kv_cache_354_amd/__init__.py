@@ -13,6 +13,8 @@ The functions carry the C names declared in ``include/pa.h``:
   host swap pool
 * ``pa_decode``       -- paged single-query decode attention
 * ``pa_decode_write`` -- ``pa_write_kv`` then ``pa_decode`` in one call
+* ``pa_decode_write_noalloc`` -- the same without a workspace, for callers
+  that cannot allocate (a static scratch array in the library serves)
 * ``pa_prefill``      -- causal paged attention of a chunk of new queries
 * ``pa_decode_workspace_bytes``
 * ``pa_pool_*`` / ``pa_seq_*`` -- host block manager (free pool, reference
@@ -85,6 +87,8 @@ _SIGS = {
                          ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
     "pa_decode_write": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp,
                                _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _sz, _vp, _i32, _vp]),
+    "pa_decode_write_noalloc": (_i32, [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache),
+                                       _vp, _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _i32, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp,
                           _i32, ctypes.c_float, _vp, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
@@ -362,6 +366,22 @@ def pa_decode_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, conte
     args, out, _ = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                 partition_size, workspace, out, out_dtype, stream, True)
     _check(load().pa_decode_write(*_new_token_args(k, v, slot_mapping, k_cache), *args))
+    return out
+
+
+# Bytes of the library's static scratch array (PA_NOALLOC_SCRATCH_BYTES).
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pa_decode_write_noalloc(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                            max_context_len, scale, out, partition_size=0, out_dtype=None, stream=None):
+    """``pa_decode_write`` for callers that cannot allocate: no workspace (the
+    library's static scratch array serves), and ``out`` must be given.
+    Calls that overlap on one GPU share that scratch and must be serialised."""
+    args, out, _ = _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, 0,
+                                None, out, out_dtype, stream, False)
+    args = args[:11] + (int(partition_size),) + args[14:]  # no workspace, no workspace size
+    _check(load().pa_decode_write_noalloc(*_new_token_args(k, v, slot_mapping, k_cache), *args))
     return out
 
 

@@ -37,6 +37,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "pa.h"
@@ -664,4 +665,67 @@ extern "C" pa_status_t pa_decode_write(const void *k, const void *v, const int64
   return decode_call(q, num_seqs, num_q_heads, k_cache, v_cache, cache, block_tables, max_blocks_per_seq,
                      context_lens, max_context_len, scale, partition_size, workspace, workspace_bytes, out,
                      out_dtype, stream, num_tokens > 0 ? &nt : nullptr);
+}
+
+// Scratch of pa_decode_write_noalloc: a static array in the code object, one
+// copy per GPU, so that entry point allocates nothing.  Host code never uses
+// the name itself as an address (on the host it is only a stand-in): each
+// device's address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+
+// Address of the current device's scratch array, or NULL (status in *err).
+void *scratch_address(pa_status_t *err) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = pa::fail(PA_EHIP, "pa_decode_write_noalloc: no usable current device (%d)", dev);
+    return nullptr;
+  }
+  void *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *err = pa::fail(PA_EHIP, "pa_decode_write_noalloc: scratch address on device %d: %s", dev,
+                    hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(p, std::memory_order_release);  // same value if two threads race here
+  return p;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_decode_write_noalloc(const void *k, const void *v, const int64_t *slot_mapping,
+                                               int32_t num_tokens, const void *q, int32_t num_seqs,
+                                               int32_t num_q_heads, void *k_cache, void *v_cache,
+                                               const pa_cache_t *cache, const int32_t *block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                               int32_t max_context_len, float scale, int32_t partition_size,
+                                               void *out, int32_t out_dtype, void *stream) {
+  if (!cache) return pa::fail(PA_EINVAL, "pa_decode_write_noalloc: cache descriptor is NULL");
+  if (partition_size != 0 && num_seqs > 0) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                                  max_context_len, partition_size);
+    if (need > PA_NOALLOC_SCRATCH_BYTES)
+      return pa::fail(PA_EINVAL,
+                      "pa_decode_write_noalloc: this call needs %zu bytes of scratch, more than the %zu of "
+                      "the library's static array (use pa_decode_write with a workspace)",
+                      need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  }
+  void *ws = nullptr;
+  size_t ws_bytes = 0;
+  if (partition_size != 0 && num_seqs > 0) {
+    pa_status_t err = PA_OK;
+    ws = scratch_address(&err);
+    if (!ws) return err;
+    ws_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
+  return pa_decode_write(k, v, slot_mapping, num_tokens, q, num_seqs, num_q_heads, k_cache, v_cache, cache,
+                         block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, partition_size,
+                         ws, ws_bytes, out, out_dtype, stream);
 }
