@@ -138,6 +138,8 @@ def parse_args(argv=None):
     p.add_argument("--separate-write", action="store_true",
                    help="pa_write_kv then pa_decode instead of one pa_decode_write call")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
+    p.add_argument("--block-size", type=int, default=16,
+                   help="waste workloads: tokens per KV block of the paged run (the block-size knob)")
     return p.parse_args(argv)
 
 
@@ -883,6 +885,7 @@ def waste_main(args):
     import paged_kv_cache_354_amd as pkv
 
     case = WASTE_WORKLOADS[args.workload]()
+    case.block_size = args.block_size
     args_c = (case.capacity, case.block_size, case.prompt_lens, case.output_lens, case.reserve_lens)
     res, secs = {}, {}
     for mode in ("contiguous", "paged"):
