@@ -1,0 +1,116 @@
+"""Register, scratch and LDS budgets of the built kernels (CPU only).
+
+The decode and prefill launch designs count on occupancy that a compiler
+change or an innocent-looking edit can silently lose: the balanced decode
+grid is one workgroup per resident slot, three 4-wave workgroups per CU,
+and the prefill kernel hides its LDS latency with three workgroups per CU.
+On gfx950 a SIMD holds 512 unified (arch + accumulation) VGPRs per lane,
+allocated in granules of 8, and a CU has 160 KiB of LDS; each 4-wave
+workgroup puts one wave on each of the CU's four SIMDs.  These tests read
+the kernel descriptors' metadata from the code objects of the library built
+here (an ELF note per code object) and check:
+
+- no kernel uses scratch (private segment) or spills VGPRs;
+- the two kernels above keep three workgroups per CU at the Llama-3-8B
+  shape (head_dim 128, four query heads per KV head).
+"""
+
+import os
+import shutil
+import struct
+import subprocess
+
+import pytest
+import yaml
+
+from paged_kv_cache_354_amd.build import LIB
+
+LLVM = "/opt/rocm/llvm/bin"
+SIMD_VGPRS, VGPR_GRANULE, CU_LDS = 512, 8, 160 * 1024
+BUNDLE_MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
+
+
+def _tool(name):
+    path = os.path.join(LLVM, name)
+    return path if os.path.exists(path) else shutil.which(name)
+
+
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    objcopy, readelf = _tool("llvm-objcopy"), _tool("llvm-readelf")
+    if not os.path.exists(LIB) or not objcopy or not readelf:
+        pytest.skip("libpagedkv.so or the LLVM binary tools are not available")
+    tmp = tmp_path_factory.mktemp("code_objects")
+    fat = tmp / "fatbin"
+    subprocess.run([objcopy, f"--dump-section=.hip_fatbin={fat}", LIB, str(tmp / "stripped.so")], check=True)
+    data = fat.read_bytes()
+    # offload bundles, one per HIP source: magic, entry count, then
+    # (offset, size, triple length, triple) per entry, offsets from the magic
+    meta = {}
+    start = data.find(BUNDLE_MAGIC)
+    while start >= 0:
+        (count,) = struct.unpack_from("<Q", data, start + len(BUNDLE_MAGIC))
+        p = start + len(BUNDLE_MAGIC) + 8
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", data, p)
+            triple = data[p + 24:p + 24 + tlen].decode()
+            p += 24 + tlen
+            if not triple.endswith("gfx950") or size == 0:
+                continue
+            co = tmp / f"co_{start}.elf"
+            co.write_bytes(data[start + off:start + off + size])
+            notes = subprocess.run([readelf, "--notes", str(co)], check=True, capture_output=True, text=True).stdout
+            doc = yaml.safe_load(notes[notes.index("---"):notes.rindex("...")])
+            for k in doc["amdhsa.kernels"]:
+                meta[k[".name"]] = k
+        start = data.find(BUNDLE_MAGIC, start + 1)
+    assert meta, "no gfx950 code objects in libpagedkv.so"
+    return meta
+
+
+def _find(kernels, *parts):
+    hits = [k for n, k in kernels.items() if all(p in n for p in parts)]
+    assert hits, f"no kernel named with {parts}"
+    return hits
+
+
+def workgroups_per_cu(k, dyn_lds=0, waves=4):
+    total = -(-k[".vgpr_count"] // VGPR_GRANULE) * VGPR_GRANULE  # arch (aligned) + accumulation VGPRs
+    by_vgpr = SIMD_VGPRS // total * 4 // waves
+    by_lds = CU_LDS // (k[".group_segment_fixed_size"] + dyn_lds)
+    return min(by_vgpr, by_lds)
+
+
+def test_no_scratch_and_no_vgpr_spills(kernels):
+    bad = {n: (k[".private_segment_fixed_size"], k.get(".vgpr_spill_count", 0)) for n, k in kernels.items()
+           if k[".private_segment_fixed_size"] or k.get(".vgpr_spill_count", 0)}
+    assert not bad, f"kernels with scratch or VGPR spills: {bad}"
+
+
+def test_every_entry_family_is_built(kernels):
+    for family in ("write_kv_kernel", "copy_blocks_kernel", "decode_kernel", "merge_kernel", "decode_gqa_kernel",
+                   "decode_gqa_balanced", "merge_balanced_kernel", "prefill_kernel"):
+        _find(kernels, family)
+
+
+def test_balanced_decode_keeps_three_workgroups_per_cu(kernels):
+    # dynamic LDS of a 64-sequence batch: prefix sums, 4096 staged block ids,
+    # one padding byte per sequence
+    dyn = (64 + 1 + 3) // 4 * 4 * 4 + 4096 * 4 + 64
+    for k in _find(kernels, "decode_gqa_balancedILi128ELi4E"):
+        assert k[".vgpr_count"] <= 168, f"{k['.name']}: {k['.vgpr_count']} VGPRs"
+        assert workgroups_per_cu(k, dyn) >= 3, k[".name"]
+
+
+def test_prefill_keeps_three_workgroups_per_cu(kernels):
+    for k in _find(kernels, "prefill_kernelILi128ELi4E"):
+        assert workgroups_per_cu(k) >= 3, f"{k['.name']}: {k['.vgpr_count']} VGPRs, " \
+                                          f"{k['.group_segment_fixed_size']} B LDS"
+
+
+def test_occupancy_model_reads_metadata_as_expected():
+    # 168 unified VGPRs fit three waves per SIMD, 176 only two; LDS binds
+    # when three workgroups' shares exceed 160 KiB
+    assert workgroups_per_cu({".vgpr_count": 168, ".group_segment_fixed_size": 1024}) == 3
+    assert workgroups_per_cu({".vgpr_count": 169, ".group_segment_fixed_size": 1024}) == 2
+    assert workgroups_per_cu({".vgpr_count": 64, ".group_segment_fixed_size": 60 * 1024}) == 2

@@ -142,31 +142,80 @@ def test_argument_errors(gpu_lib):
 
 
 @pytest.mark.parametrize("name", ["prefill_llama3_8b", "prefill_chunked"])
-def test_full_size_sampled(gpu_lib, name):
+def test_full_size_every_row(gpu_lib, name):
     """The benchmarked prefill step (store the chunk's tokens, then attend) at
-    full size; sampled rows against the oracle (each row is one query's
-    softmax over its visible keys)."""
+    full size: every (query, head) row against the oracle (fp32 output within
+    the derived bound; bf16 output bitwise the fp32 output rounded to nearest
+    even).  The oracle runs sequence by sequence on threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import kvcache as KV
+
+    from gpu_cases import check_bf16_is_rounded_f32
+
     pc = W.c6_prefill_llama8b() if name == "prefill_llama3_8b" else W.c6_chunked_prefill()
     c = pc.case
     announce("prefill full", name)
     dc = DevCase(c)
     gpu_lib.pa_write_kv(to_dev(pc.k_new), to_dev(pc.v_new), to_dev(pc.slot_mapping), dc.k_cache, dc.v_cache)
-    out = gpu_lib.pa_prefill(to_dev(pc.q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
-                             to_dev(pc.cu_seqlens), pc.max_query_len, c.max_context, c.scale,
-                             out_dtype=torch.float32).cpu().numpy().astype(np.float64)
-    del dc
+    args = (to_dev(pc.q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, to_dev(pc.cu_seqlens),
+            pc.max_query_len, c.max_context, c.scale)
+    o32 = gpu_lib.pa_prefill(*args, out_dtype=torch.float32)
+    obf = gpu_lib.pa_prefill(*args)
+    torch.cuda.synchronize()
+    check_bf16_is_rounded_f32(obf, o32)
+    out = o32.cpu().numpy().astype(np.float64)
+    del dc, o32, obf
     torch.cuda.empty_cache()
-    from oracle import kvcache as KV
     kc, vc = KV.write_kv(c.k_cache, c.v_cache, pc.k_new, pc.v_new, pc.slot_mapping, c.block_size)
     vmax = float(np.max(np.abs(out_to_f64_np(vc))))
-    grp = c.num_q_heads // c.num_kv_heads
-    rng = np.random.default_rng(21)
-    picks = rng.integers(0, pc.num_tokens, 40)
-    seq_of = np.searchsorted(pc.cu_seqlens, picks, side="right") - 1
-    for row, s in zip(picks, seq_of):
-        n = int(pc.cu_seqlens[s + 1] - pc.cu_seqlens[s])
-        pos = int(c.context_lens[s]) - n + int(row - pc.cu_seqlens[s])
-        for h in (0, int(rng.integers(c.num_q_heads))):
-            ref = P.prefill_row(pc.q[row, h], kc, vc, c.block_tables[s], c.context_lens[s], pos, c.scale, W.BF16,
-                                h // grp)
-            check_prefill(out[row, h], ref, vmax, bf16_out=False)
+    cu = pc.cu_seqlens
+    announce("prefill full", name, "oracle over", int(cu[-1]), "query rows")
+
+    def oracle_seq(s):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        return P.prefill(pc.q[rows], kc, vc, c.block_tables[s:s + 1], c.context_lens[s:s + 1],
+                         np.array([0, cu[s + 1] - cu[s]], np.int32), c.scale, W.BF16)
+
+    with ThreadPoolExecutor(16) as ex:
+        ref = np.concatenate(list(ex.map(oracle_seq, range(c.num_seqs))), axis=0)
+    check_prefill(out, ref, vmax, bf16_out=False)
+
+
+@pytest.mark.parametrize("d,bs", [(128, 16), (128, 1), (64, 32)])
+def test_needles_strict(gpu_lib, d, bs):
+    """q = 0 makes every visible weight exactly 1, so with one-hot value rows
+    (key t has a 1 in channel t % d) each output is the exact ratio of the
+    visible keys in a channel to all visible keys: the causal mask, the gather
+    through the table and the tails are checked to fp32 division rounding
+    (1e-6 relative), far tighter than the bf16-weight bound.  Poisoned pools:
+    NaN in every slot no sequence attends to."""
+    rng = np.random.default_rng(d + bs)
+    lens = [1, 16, 17, 100, 333, 777, 40]
+    nq = [1, 16, 5, 100, 64, 300, 0]
+    case = W.make_case(f"needles_{d}_{bs}", seed=int(rng.integers(1 << 20)), dtype=W.BF16, context_lens=lens,
+                       num_q_heads=32, num_kv_heads=8, head_dim=d, block_size=bs, poison=True)
+    one = W.round_to_bf16(np.ones(1, np.float32))[0]
+    for s, ctx in enumerate(lens):
+        for t in range(ctx):
+            blk, off = int(case.block_tables[s, t // bs]), t % bs
+            case.v_cache[blk, :, off, :] = 0
+            case.v_cache[blk, :, off, t % d] = one
+        blk, off = int(case.block_tables[s, (ctx - 1) // bs]), (ctx - 1) % bs
+        case.k_cache[blk, :, off, :] = case.k_new[s]  # the newest key's slot was poisoned
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = np.zeros((int(cu[-1]), 32, d), np.uint16)
+    dc = DevCase(case)  # every position already in the pools: no store
+    announce("needles", d, bs)
+    out = gpu_lib.pa_prefill(to_dev(q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, to_dev(cu),
+                             int(max(nq)), case.max_context, case.scale, out_dtype=torch.float32)
+    got = out.cpu().numpy().astype(np.float64)
+    ref = P.prefill(q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, cu, case.scale, W.BF16)
+    # closed form, independent of the oracle: row i of sequence s sees keys 0 .. ctx - n + i
+    for s, (ctx, n) in enumerate(zip(lens, nq)):
+        for i in range(n):
+            seen = ctx - n + i + 1
+            counts = np.bincount(np.arange(seen) % d, minlength=d)
+            np.testing.assert_allclose(ref[cu[s] + i], np.broadcast_to(counts / seen, (32, d)), rtol=1e-12, atol=0)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, ref, rtol=1e-6, atol=0)
