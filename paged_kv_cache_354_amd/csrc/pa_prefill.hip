@@ -33,6 +33,12 @@
 // combined over the 4 lanes that share a row (lanes n, n+16, n+32, n+48).
 // The probabilities enter the PV product in bf16 (the usual flash-attention
 // trade: relative error up to 2^-9 per weight), the rest is fp32.
+//
+// Two kernels share that tile math and differ in how the key/value tiles
+// reach LDS.  prefill_ring_kernel (head_dim 128, blocks of 8 tokens or more)
+// loads them straight from HBM into a ring of three LDS slots, two tiles
+// ahead; prefill_kernel (the other shapes) loads the next tile into
+// registers during the current tile's math and stores it to LDS after.
 
 #include <hip/hip_runtime.h>
 
@@ -96,42 +102,41 @@ struct PrefillShared {
   int32_t tbl[kTblLds];                // block ids of keys [0, kend)
 };
 
-template <int D, int G>
-// Three workgroups per CU (see the operand reads in the tile loop).
-__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
-  constexpr int GW = G < 4 ? G : 4;   // query heads per workgroup
-  constexpr int TQ = 16 * kRB * (4 / GW);  // query tokens per workgroup
-  constexpr int HG = G / GW;          // workgroups per (KV head, query block)
-  constexpr int C = D / 8;            // 16-byte chunks per row
-  constexpr int KSTEPS = D / 32;
-  constexpr int OB = D / 16;          // 16-channel blocks of the output
-  __shared__ PrefillShared<D> sh;
 
-  // Work order: query block (last first: causal blocks near the end see the
-  // most keys), sequence (longest context first), head group, KV head;
-  // contiguous ranges per XCD.  With the KV head slowest, XCD x takes the
-  // same KV head(s) of every sequence: the XCDs get equal shares however
-  // unequal the sequences are, and an XCD's L2 holds the keys and values of
-  // its own heads only.  Longest first within an XCD keeps a long
-  // sequence's workgroups from starting last and running alone at the end.
+// Which (sequence, query block, head group, KV head) workgroup blockIdx.x
+// serves, and the sequence's query offset, query count and context length.
+//
+// Work order: query block (last first: causal blocks near the end see the
+// most keys), sequence (longest context first), head group, KV head;
+// contiguous ranges per XCD.  With the KV head slowest, XCD x takes the
+// same KV head(s) of every sequence: the XCDs get equal shares however
+// unequal the sequences are, and an XCD's L2 holds the keys and values of
+// its own heads only.  Longest first within an XCD keeps a long
+// sequence's workgroups from starting last and running alone at the end.
+struct WorkItem {
+  int s, lo, n, ctx;  // sequence, its first query row, its query rows, its context length
+  int qb, hg, kvh;    // query block, head group, KV head
+};
+
+template <int HG>
+__device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scratch) {
+  WorkItem w;
   const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
   int r = xcd_work_id(blockIdx.x, n_work);
-  const int qb = a.q_blocks - 1 - r % a.q_blocks;
+  w.qb = a.q_blocks - 1 - r % a.q_blocks;
   r /= a.q_blocks;
   const int rank = r % a.num_seqs;
   r /= a.num_seqs;
-  const int hg = r % HG;
-  const int kvh = r / HG;
-  int s = rank, lo, n, ctx;
+  w.hg = r % HG;
+  w.kvh = r / HG;
   if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
     // the sequence of this rank by context length, longest first, ties by
     // index (a permutation, so exactly one sequence has it).  The lengths
     // and the query offsets are staged together, so the choice costs no
-    // extra round trip; sh.tbl is scratch here (the block ids are staged
-    // into it below).
+    // extra round trip; the scratch is LDS the caller reuses afterwards.
     __shared__ int chosen;
-    int32_t *len = sh.tbl;
-    int32_t *cu = sh.tbl + kRankSeqs;
+    int32_t *len = scratch;
+    int32_t *cu = scratch + kRankSeqs;
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
       cu[i] = a.cu_seqlens[i];
       if (i < a.num_seqs) {
@@ -150,18 +155,196 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
       if (rk == rank) chosen = t;
     }
     __syncthreads();
-    s = chosen;
-    lo = cu[s];
-    n = cu[s + 1] - lo;
-    ctx = len[s];
+    w.s = __builtin_amdgcn_readfirstlane(chosen);
+    w.lo = __builtin_amdgcn_readfirstlane(cu[w.s]);
+    w.n = __builtin_amdgcn_readfirstlane(cu[w.s + 1]) - w.lo;
+    w.ctx = __builtin_amdgcn_readfirstlane(len[w.s]);
     __syncthreads();  // every thread has read the scratch before it is overwritten
   } else {
-    lo = a.cu_seqlens[s];
-    n = a.cu_seqlens[s + 1] - lo;
-    ctx = a.context_lens[s];
-    ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+    w.s = rank;
+    w.lo = a.cu_seqlens[w.s];
+    w.n = a.cu_seqlens[w.s + 1] - w.lo;
+    const int c = a.context_lens[w.s];
+    w.ctx = c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
   }
-  const int q0 = qb * TQ;
+  return w;
+}
+
+// One tile of 32 keys for the wave's 2 x 16 rows: scores, online softmax,
+// and the product with V, on the matrix cores.  kop_at(hh, i) returns the A
+// operand of S^T for keys 16hh.. (channels [8(4i + g), +8) of key row
+// 16hh + nl); vop_at(j) returns the V^T operand of channel block j (see the
+// file comment).  row0 is the position of the wave's first row; prow[rb]
+// the position of this lane's row of block rb (-1 for no row).
+template <int D, typename KOp, typename VOp>
+__device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 (&qop)[kRB][D / 32],
+                                            f32x4_t (&o)[kRB][D / 16], float (&m)[kRB], float (&l)[kRB],
+                                            const int (&prow)[kRB], int kt0, int row0, int g, float qscale,
+                                            int xor16, int xor32) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int OB = D / 16;
+  __builtin_amdgcn_s_setprio(0);
+  // S^T for the two 16-key halves of both row blocks; each K operand
+  // read from LDS feeds both blocks.  A half's K operands are read just
+  // before its products and the V^T operands just before theirs (below):
+  // holding all of a tile's operands at once took 200 VGPRs and two
+  // workgroups per CU; read this way the kernel fits three (164 VGPRs),
+  // whose waves hide the LDS latency instead (measured on MI355X: 8 whole
+  // prompts 519 -> 483 us, 512-token chunks 783 -> 769 us).
+  f32x4_t st[kRB][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    bf16x8_t kop[KSTEPS];
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) kop[i] = kop_at(hh, i);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) st[rb][hh] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i)
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        st[rb][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], __builtin_bit_cast(bf16x8_t, qop[rb][i]),
+                                                             st[rb][hh], 0, 0, 0);
+  }
+  // Two waves share each SIMD: a wave in its softmax (a chain of vector
+  // instructions) runs at a higher priority than one issuing matrix ops,
+  // so it gets through and reaches its own matrix ops sooner while the
+  // other's are in the pipeline (measured on MI355X: 1.3-1.5% faster;
+  // the opposite, or raising it already at the V^T reads, was not).
+  __builtin_amdgcn_s_setprio(2);
+  // Per row block: causal mask (only where the tile reaches past the
+  // block's first row), reference max, probabilities.
+  bf16x8_t pb[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const bool diag = kt0 + kKeys - 1 > row0 + 16 * rb;  // wave-uniform
+    // raw scores; the scale (positive) enters through the max and the
+    // exponent's fma
+    float z[8];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[4 * hh + e] = st[rb][hh][e];
+    if (diag) {
+      // A real branch: most tiles lie wholly below the block's first row,
+      // and the compiler would otherwise turn the mask into selects that
+      // every tile pays for (an empty volatile asm cannot be speculated).
+      asm volatile("");
+      // key kt0 + 16hh + 4g + e lies past the row when 16hh + e > lim
+      const int lim = prow[rb] - kt0 - 4 * g;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (16 * hh + e > lim) z[4 * hh + e] = -INFINITY;
+    }
+    // maximum (NaN-propagating) takes matrix-core results as they are;
+    // fmaxf would first quiet each of them, one more instruction each
+    float mx = z[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
+    mx *= qscale;
+    // The reference max m moves only when some score passes it by more
+    // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
+    // 2^kLazyMax, and the rescale of O^T is rare after the first tiles.
+    // The test needs only this lane's max; inside, every row takes the
+    // max over its 4 lanes, so the 4 lanes of a row keep one m.  The
+    // result does not depend on m.
+    if (__any(mx > m[rb] + kLazyMax)) {
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
+      mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
+      const float mn = fmaxf(m[rb], mx);
+      const float alpha = exp2_fast(m[rb] - mn);
+      m[rb] = mn;
+      l[rb] *= alpha;
+#pragma unroll
+      for (int j = 0; j < OB; ++j) o[rb][j] *= alpha;
+    }
+    f32x8_t p;
+    const float negm = -m[rb];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], qscale, negm));
+    float ps = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) ps += p[e];
+    l[rb] += ps;
+    pb[rb] = __builtin_convertvector(p, bf16x8_t);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
+#pragma unroll
+  for (int j = 0; j < OB; ++j) {
+    const bf16x8_t vop = vop_at(j);
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[rb], o[rb][j], 0, 0, 0);
+  }
+}
+
+// Row sums over each row's 4 lanes; the normalised rows of the wave.
+template <int D>
+__device__ __forceinline__ void store_rows(const PrefillArgs &a, const f32x4_t (&o)[kRB][D / 16],
+                                           const float (&l)[kRB], const bool (&row_ok)[kRB], int lo, int tok0,
+                                           int h, int nl, int g) {
+  constexpr int OB = D / 16;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    float lr = l[rb];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    if (row_ok[rb]) {
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+      const size_t base = ((size_t)(lo + tok0 + 16 * rb + nl) * a.num_q_heads + h) * D + 4 * g;
+#pragma unroll
+      for (int j = 0; j < OB; ++j) {
+        const f32x4_t v = o[rb][j] * inv;
+        if (a.out_f32) {
+          *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + 16 * j) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          const uint32_t w0 = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
+          const uint32_t w1 = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base + 16 * j) = make_uint2(w0, w1);
+        }
+      }
+    }
+  }
+}
+
+// The wave's rows, their positions, and their query operands.
+template <int D>
+struct WaveRows {
+  int prow[kRB];       // position of the lane's row of block rb (-1: no row)
+  bool row_ok[kRB];
+  uint4 qop[kRB][D / 32];  // B operands of S^T: channels [8(4i + g), +8) of each row's query
+
+  __device__ __forceinline__ void load(const PrefillArgs &a, int lo, int n, int first_pos, int tok0, int h,
+                                       int nl, int g) {
+    constexpr int C = D / 8;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      const int tok = tok0 + 16 * rb + nl;
+      row_ok[rb] = tok < n;
+      prow[rb] = row_ok[rb] ? first_pos + tok : -1;
+      const uint4 *qrow = a.q + ((size_t)(lo + (row_ok[rb] ? tok : 0)) * a.num_q_heads + h) * C + g;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) qop[rb][i] = row_ok[rb] ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
+    }
+  }
+};
+
+template <int D, int G>
+// Three workgroups per CU (see the operand reads in the tile loop).
+__global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
+  constexpr int GW = G < 4 ? G : 4;   // query heads per workgroup
+  constexpr int TQ = 16 * kRB * (4 / GW);  // query tokens per workgroup
+  constexpr int HG = G / GW;          // workgroups per (KV head, query block)
+  constexpr int C = D / 8;            // 16-byte chunks per row
+  constexpr int OB = D / 16;          // 16-channel blocks of the output
+  __shared__ PrefillShared<D> sh;
+
+  const WorkItem wk = find_work<HG>(a, sh.tbl);
+  const int s = wk.s, lo = wk.lo, n = wk.n, ctx = wk.ctx, kvh = wk.kvh;
+  const int q0 = wk.qb * TQ;
   if (q0 >= n) return;
   const int first_pos = ctx - n;  // position of query 0 of the sequence
 
@@ -173,26 +356,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   // byte addresses of the lanes 16 and 32 away (the 4 lanes of a row)
   const int xor16 = (lane ^ 16) << 2;
   const int xor32 = (lane ^ 32) << 2;
-  const int h = kvh * G + hg * GW + wave % GW;
+  const int h = kvh * G + wk.hg * GW + wave % GW;
   const int tok0 = q0 + (wave / GW) * 16 * kRB;  // the wave's first query
   // keys the workgroup needs, and the ones this wave needs
   const int kend = max(0, min(ctx, first_pos + min(q0 + TQ, n)));
   const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16 * kRB, n))) : 0;
 
-  // The lane's rows (query tok0 + 16r + nl, head h) and their last visible keys.
-  int prow[kRB];
-  bool row_ok[kRB];
-  // B operands of S^T: channels [8(4i + g), +8) of each row's query.
-  uint4 qop[kRB][KSTEPS];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int tok = tok0 + 16 * rb + nl;
-    row_ok[rb] = tok < n;
-    prow[rb] = row_ok[rb] ? first_pos + tok : -1;
-    const uint4 *qrow = a.q + ((size_t)(lo + (row_ok[rb] ? tok : 0)) * a.num_q_heads + h) * C + g;
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) qop[rb][i] = row_ok[rb] ? qrow[4 * i] : make_uint4(0, 0, 0, 0);
-  }
+  WaveRows<D> rows;
+  rows.load(a, lo, n, first_pos, tok0, h, nl, g);
 
   f32x4_t o[kRB][OB];  // O^T: channel 16j + 4g + e of row nl of block rb
 #pragma unroll
@@ -323,112 +494,21 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
     const int kt0 = t * kKeys;
     if (t + 1 < ntiles) load_tile(kt0 + kKeys);  // in flight during this tile's math
     if (kt0 < wkend) {
-      __builtin_amdgcn_s_setprio(0);
-      // S^T for the two 16-key halves of both row blocks; each K operand
-      // read from LDS feeds both blocks.  A half's K operands are read just
-      // before its products and the V^T operands just before theirs (below):
-      // holding all of a tile's operands at once took 200 VGPRs and two
-      // workgroups per CU; read this way the kernel fits three (164 VGPRs),
-      // whose waves hide the LDS latency instead (measured on MI355X: 8 whole
-      // prompts 519 -> 483 us, 512-token chunks 783 -> 769 us).
-      f32x4_t st[kRB][2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8_t kop[KSTEPS];
-#pragma unroll
-        for (int i = 0; i < KSTEPS; ++i) kop[i] = __builtin_bit_cast(bf16x8_t, sh.k[b][16 * hh + nl][4 * i + g]);
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) st[rb][hh] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int i = 0; i < KSTEPS; ++i)
-#pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            st[rb][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], __builtin_bit_cast(bf16x8_t, qop[rb][i]),
-                                                                 st[rb][hh], 0, 0, 0);
-      }
-      // Two waves share each SIMD: a wave in its softmax (a chain of vector
-      // instructions) runs at a higher priority than one issuing matrix ops,
-      // so it gets through and reaches its own matrix ops sooner while the
-      // other's are in the pipeline (measured on MI355X: 1.3-1.5% faster;
-      // the opposite, or raising it already at the V^T reads, was not).
-      __builtin_amdgcn_s_setprio(2);
-      // Per row block: causal mask (only where the tile reaches past the
-      // block's first row), reference max, probabilities.
-      bf16x8_t pb[kRB];
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const bool diag = kt0 + kKeys - 1 > first_pos + tok0 + 16 * rb;  // wave-uniform
-        // raw scores; the scale (positive) enters through the max and the
-        // exponent's fma
-        float z[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[4 * hh + e] = st[rb][hh][e];
-        if (diag) {
-          // A real branch: most tiles lie wholly below the block's first row,
-          // and the compiler would otherwise turn the mask into selects that
-          // every tile pays for (an empty volatile asm cannot be speculated).
-          asm volatile("");
-          // key kt0 + 16hh + 4g + e lies past the row when 16hh + e > lim
-          const int lim = prow[rb] - kt0 - 4 * g;
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (16 * hh + e > lim) z[4 * hh + e] = -INFINITY;
-        }
-        // maximum (NaN-propagating) takes matrix-core results as they are;
-        // fmaxf would first quiet each of them, one more instruction each
-        float mx = z[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
-        mx *= a.qscale;
-        // The reference max m moves only when some score passes it by more
-        // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
-        // 2^kLazyMax, and the rescale of O^T is rare after the first tiles.
-        // The test needs only this lane's max; inside, every row takes the
-        // max over its 4 lanes, so the 4 lanes of a row keep one m.  The
-        // result does not depend on m.
-        if (__any(mx > m[rb] + kLazyMax)) {
-          mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
-          mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
-          const float mn = fmaxf(m[rb], mx);
-          const float alpha = exp2_fast(m[rb] - mn);
-          m[rb] = mn;
-          l[rb] *= alpha;
-#pragma unroll
-          for (int j = 0; j < OB; ++j) o[rb][j] *= alpha;
-        }
-        f32x8_t p;
-        const float negm = -m[rb];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], a.qscale, negm));
-        float ps = p[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) ps += p[e];
-        l[rb] += ps;
-        pb[rb] = __builtin_convertvector(p, bf16x8_t);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
       // V^T operand of channel block j: lane (g, n) names key rows 4g + n / 4
       // and 16 + 4g + n / 4 at channels 16j + 4 (n % 4) .. + 3, and receives
       // channel 16j + n of keys 4g..4g+3 and 16+4g..16+4g+3.
-      {
-        constexpr int VS = D + 16;  // elements per V row in LDS
-        const uint16_t *vb = reinterpret_cast<const uint16_t *>(&sh.v[b][0][0]);
-        const int off0 = (4 * g + (nl >> 2)) * VS + 4 * (nl & 3);
-#pragma unroll
-        for (int j = 0; j < OB; ++j) {
-          const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * j));
-          const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * VS + 16 * j));
-          const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-            o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[rb], o[rb][j], 0, 0, 0);
-        }
-      }
+      constexpr int VS = D + 16;  // elements per V row in LDS
+      const uint16_t *vb = reinterpret_cast<const uint16_t *>(&sh.v[b][0][0]);
+      const int off0 = (4 * g + (nl >> 2)) * VS + 4 * (nl & 3);
+      attend_tile<D>(
+          [&](int hh, int i) { return __builtin_bit_cast(bf16x8_t, sh.k[b][16 * hh + nl][4 * i + g]); },
+          [&](int j) {
+            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * j));
+            const s16x4_t hi4 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vb + off0 + 16 * VS + 16 * j));
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          },
+          rows.qop, o, m, l, rows.prow, kt0, first_pos + tok0, g, a.qscale, xor16, xor32);
     }
     __builtin_amdgcn_s_setprio(0);
     if (t + 1 < ntiles) store_tile(b ^ 1, kt0 + kKeys);
@@ -438,34 +518,211 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   if (tbl_lds) run(std::true_type{});
   else run(std::false_type{});
 
-  // Row sums over the row's 4 lanes; normalised output.
+  store_rows<D>(a, o, l, rows.row_ok, lo, tok0, h, nl, g);
+}
+
+// ---- The ring pipeline (head_dim 128, block size >= 8) ----
+//
+// Tiles reach LDS without passing through registers: each wave issues
+// global_load_lds_dwordx4 (64 lanes x 16 bytes straight into LDS at M0 +
+// 16 x lane) for 8 key rows of K and of V per tile, two tiles ahead, into a
+// ring of three tile slots.  Compared with loading the next tile into
+// registers and storing it after the math, this frees the 16 staging VGPRs
+// and the per-tile address arithmetic, and gives each load two tiles of
+// math to arrive in (measured on MI355X: a build that skipped the loads
+// altogether ran 10-17% faster, the bound of what hiding them can win).
+//
+// The compiler does not follow these loads: they are issued from inline
+// assembly, which writes no register, and the waits on them are explicit
+// (vmcnt counts this wave's loads in the order it issued them; nothing else
+// the compiler tracks is in flight inside the tile loop).  The block ids
+// come from scalar loads through the constant address space (the table is
+// not written during the call), so they use the scalar counter and keep
+// the vector count to the tiles alone.
+//
+// LDS image of a tile: K and V as 8 groups of 4 key rows each.  A group is
+// one load instruction.  Each quad of lanes (4 consecutive lanes, which the
+// vector memory path serves together) brings 64 contiguous bytes of one
+// row: quad 4s + r loads segment s (bytes 64s..64s+63) of row r, so a group
+// is stored segment-major (segment s of row r at 256 s + 64 r), and groups
+// sit 1056 bytes apart (32 bytes of padding).  A quad that spans 4 rows
+// instead touched 4 cache lines per quad: 2.9x the vector L1 accesses and
+// 11% slower.  Laid out this way, the K operand reads (rows nl, chunk
+// 4i + g) of the lanes the LDS serves together (0-7 with 16-23) and the V^T
+// transposing reads of lanes 0-31 fall in 64 different banks, and every
+// read of the tile math is a lane constant plus an immediate.
+constexpr int kRing = 3;         // tile slots: the one in use and the next two
+constexpr int kGrp = 1056;       // bytes from one group to the next
+constexpr int kSlotK = 8 * kGrp;
+constexpr int kSlot = 2 * kSlotK;  // bytes per tile slot (K, then V)
+constexpr int kRowBytes = 256;   // one bf16 row of 128 channels
+// s_waitcnt operand: vmcnt(4) (one tile of this wave's loads may stay in flight)
+constexpr int kWaitVmem4 = 0x0F74;
+
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane.  M0 holds
+// the LDS address (the compiler uses M0 for nothing in these kernels; it is
+// declared clobbered all the same, which clang notes as a reserved register).
+// One wait state between the M0 write and the load that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(uint64_t base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
+}
+
+template <int G>
+// Three workgroups per CU: 3 x 50,688 bytes of ring fit the 160 KiB of LDS.
+__global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a) {
+  constexpr int D = 128;
+  constexpr int GW = G < 4 ? G : 4;   // query heads per workgroup
+  constexpr int TQ = 16 * kRB * (4 / GW);  // query tokens per workgroup
+  constexpr int HG = G / GW;          // workgroups per (KV head, query block)
+  constexpr int OB = D / 16;          // 16-channel blocks of the output
+  __shared__ uint4 ring[kRing * kSlot / 16];
+
+  const WorkItem wk = find_work<HG>(a, reinterpret_cast<int32_t *>(ring));
+  const int s = wk.s, lo = wk.lo, n = wk.n, ctx = wk.ctx, kvh = wk.kvh;
+  const int q0 = wk.qb * TQ;
+  if (q0 >= n) return;
+  const int first_pos = ctx - n;  // position of query 0 of the sequence
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;
+  const int nl = lane & 15;
+  const int xor16 = (lane ^ 16) << 2;
+  const int xor32 = (lane ^ 32) << 2;
+  const int h = kvh * G + wk.hg * GW + wave % GW;
+  const int tok0 = q0 + (wave / GW) * 16 * kRB;  // the wave's first query
+  // keys the workgroup needs, and the ones this wave needs
+  const int kend = max(0, min(ctx, first_pos + min(q0 + TQ, n)));
+  const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16 * kRB, n))) : 0;
+
+  WaveRows<D> rows;
+  rows.load(a, lo, n, first_pos, tok0, h, nl, g);
+
+  f32x4_t o[kRB][OB];  // O^T: channel 16j + 4g + e of row nl of block rb
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int j = 0; j < OB; ++j) o[rb][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m[kRB], l[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    float lr = l[rb];
-    lr += __shfl_xor(lr, 16, 64);
-    lr += __shfl_xor(lr, 32, 64);
-    if (row_ok[rb]) {
-      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
-      const size_t base = ((size_t)(lo + tok0 + 16 * rb + nl) * a.num_q_heads + h) * D + 4 * g;
+    m[rb] = kNegBig;
+    l[rb] = 0.0f;
+  }
+  // The query rows have arrived before any tile load is issued: from here
+  // on, vmcnt counts this wave's tile loads only.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+
+  const_i32 *trow = (const_i32 *)(a.block_tables + (size_t)s * a.max_blocks);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
+  const uint64_t block_bytes = (uint64_t)(uint32_t)(a.num_kv_heads * a.block_size) * kRowBytes;
+  const uint64_t head_bytes = (uint64_t)kvh * a.block_size * kRowBytes;
+  const uint64_t kbase = (uint64_t)(uintptr_t)a.k_cache + head_bytes;
+  const uint64_t vbase = (uint64_t)(uintptr_t)a.v_cache + head_bytes;
+  const uint32_t lane_off = ((lane >> 2) & 3) * kRowBytes + (lane >> 4) * 64 + (lane & 3) * 16;
+  const int bmask = a.block_size - 1;
+
+  // The table entry of group grp (keys 32u + 8 wave + 4 grp ..) of tile u.
+  // A group's 4 keys share a block (block size >= 8, groups 4-aligned).
+  // The entry is clamped into the pool where it is used, so that the wait
+  // for the scalar load falls there, a tile later.
+  auto block_of = [&](int u, int grp) -> int {
+    const int key0 = min(u * kKeys + 8 * wave + 4 * grp, kend - 1);
+    return trow[key0 >> a.log2_bs];
+  };
+  // This wave's loads of tile u (4 instructions): its two groups of K and V.
+  // Keys at or past kend read key kend - 1 instead (a real key, finite; the
+  // causal mask gives every such key weight 0).
+  auto load_tile = [&](int u, int blk0, int blk1) {
+    const uint32_t slot = ring0 + (uint32_t)(u % kRing) * kSlot;
 #pragma unroll
-      for (int j = 0; j < OB; ++j) {
-        const f32x4_t v = o[rb][j] * inv;
-        if (a.out_f32) {
-          *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + base + 16 * j) =
-              make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-          const uint32_t w0 = (uint32_t)to_bf16(v[0]) | ((uint32_t)to_bf16(v[1]) << 16);
-          const uint32_t w1 = (uint32_t)to_bf16(v[2]) | ((uint32_t)to_bf16(v[3]) << 16);
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + base + 16 * j) = make_uint2(w0, w1);
-        }
+    for (int grp = 0; grp < 2; ++grp) {
+      const int qg = 2 * wave + grp;
+      const int kt = u * kKeys + 4 * qg;
+      int key0 = kt;
+      uint32_t voff = lane_off;
+      if (kt + 3 >= kend) {  // uniform: the group reaches kend
+        key0 = min(kt, kend - 1);
+        voff = (uint32_t)(min(kt + ((lane >> 2) & 3), kend - 1) - key0) * kRowBytes + (lane >> 4) * 64 + (lane & 3) * 16;
       }
+      const int blk = grp ? blk1 : blk0;
+      const uint32_t pb = (unsigned)blk < (unsigned)a.num_blocks ? (uint32_t)blk : 0u;  // stay inside the pool
+      const uint64_t off = (uint64_t)pb * block_bytes + (uint64_t)(key0 & bmask) * kRowBytes;
+      load_lds16(uniform64(kbase + off), voff, __builtin_amdgcn_readfirstlane(slot + qg * kGrp));
+      load_lds16(uniform64(vbase + off), voff, __builtin_amdgcn_readfirstlane(slot + kSlotK + qg * kGrp));
+    }
+  };
+
+  // Lane constants of the tile math's LDS reads (bytes from the slot).
+  // K operand (hh, i): key row 16hh + nl = group 4hh + nl / 4, row nl % 4,
+  // segment i, chunk g of the segment.  V^T operand j: lane names key row
+  // 4g + nl / 4 (and 16 + that: group g + 4) at channels 16j + 4 (nl % 4)
+  // .. + 3: segment j / 2, chunk 2 (j % 2) + (nl / 2) % 2, half nl % 2.
+  const uint32_t k_lane = (nl >> 2) * kGrp + (nl & 3) * 64 + g * 16;
+  const uint32_t v_lane = g * kGrp + (nl >> 2) * 64 + ((nl >> 1) & 1) * 16 + (nl & 1) * 8;
+  const char *ring_bytes = reinterpret_cast<const char *>(ring);
+
+  const int ntiles = (kend + kKeys - 1) / kKeys;
+  int nb0 = 0, nb1 = 0;  // block ids of the tile loaded next
+  if (ntiles > 0) load_tile(0, block_of(0, 0), block_of(0, 1));
+  if (ntiles > 1) load_tile(1, block_of(1, 0), block_of(1, 1));
+  if (ntiles > 2) {
+    nb0 = block_of(2, 0);
+    nb1 = block_of(2, 1);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t have landed (those of t + 1 may not), then
+    // every wave's have
+    if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVmem4);
+    else __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __syncthreads();
+    // tile t + 2 goes to the slot of tile t - 1, which every wave finished
+    // reading before the barrier
+    if (t + 2 < ntiles) load_tile(t + 2, nb0, nb1);
+    const int kt0 = t * kKeys;
+    if (kt0 < wkend) {
+      const char *slot = ring_bytes + (t % kRing) * kSlot;
+      attend_tile<D>(
+          [&](int hh, int i) {
+            return *reinterpret_cast<const bf16x8_t *>(slot + k_lane + hh * 4 * kGrp + i * 256);
+          },
+          [&](int j) {
+            const char *v = slot + kSlotK + v_lane + (j >> 1) * 256 + (j & 1) * 32;
+            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)v);
+            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(v + 4 * kGrp));
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          },
+          rows.qop, o, m, l, rows.prow, kt0, first_pos + tok0, g, a.qscale, xor16, xor32);
+    }
+    // The table entries of tile t + 3, read after the tile's LDS reads: the
+    // scalar loads share the LDS wait counter, and here they are waited for
+    // only at the next barrier.
+    if (t + 3 < ntiles) {
+      nb0 = block_of(t + 3, 0);
+      nb1 = block_of(t + 3, 1);
     }
   }
+  store_rows<D>(a, o, l, rows.row_ok, lo, tok0, h, nl, g);
 }
 
 template <int D, int G>
 hipError_t launch_dg(const PrefillArgs &a, int n_work, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(n_work), dim3(kThreads), 0, st, a);
+  if (D == 128 && a.block_size >= 8)
+    hipLaunchKernelGGL((prefill_ring_kernel<G>), dim3(n_work), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(n_work), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@ the kernel descriptors' metadata from the code objects of the library built
 here (an ELF note per code object) and check:
 
 - no kernel uses scratch (private segment) or spills VGPRs;
-- the two kernels above keep three workgroups per CU at the Llama-3-8B
-  shape (head_dim 128, four query heads per KV head).
+- those kernels keep three workgroups per CU at the Llama-3-8B shape
+  (head_dim 128, four query heads per KV head).
 """
 
 import os
@@ -89,7 +89,7 @@ def test_no_scratch_and_no_vgpr_spills(kernels):
 
 def test_every_entry_family_is_built(kernels):
     for family in ("write_kv_kernel", "copy_blocks_kernel", "decode_kernel", "merge_kernel", "decode_gqa_kernel",
-                   "decode_gqa_balanced", "merge_balanced_kernel", "prefill_kernel"):
+                   "decode_gqa_balanced", "merge_balanced_kernel", "prefill_kernel", "prefill_ring_kernel"):
         _find(kernels, family)
 
 
@@ -103,7 +103,9 @@ def test_balanced_decode_keeps_three_workgroups_per_cu(kernels):
 
 
 def test_prefill_keeps_three_workgroups_per_cu(kernels):
-    for k in _find(kernels, "prefill_kernelILi128ELi4E"):
+    # the ring kernel serves head_dim 128 at block sizes 8 and up, the
+    # register-staged kernel the other shapes
+    for k in _find(kernels, "prefill_ring_kernelILi4E") + _find(kernels, "prefill_kernelILi128ELi4E"):
         assert workgroups_per_cu(k) >= 3, f"{k['.name']}: {k['.vgpr_count']} VGPRs, " \
                                           f"{k['.group_segment_fixed_size']} B LDS"
 
