@@ -93,6 +93,7 @@ struct PrefillArgs {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8_t;
 
 template <int D>
 struct PrefillShared {
@@ -678,7 +679,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   // .. + 3: segment j / 2, chunk 2 (j % 2) + (nl / 2) % 2, half nl % 2.
   const uint32_t k_lane = (nl >> 2) * kGrp + (nl & 3) * 64 + g * 16;
   const uint32_t v_lane = g * kGrp + (nl >> 2) * 64 + ((nl >> 1) & 1) * 16 + (nl & 1) * 8;
-  const char *ring_bytes = reinterpret_cast<const char *>(ring);
 
   const int ntiles = (kend + kKeys - 1) / kKeys;
   int nb0 = 0, nb1 = 0;  // block ids of the tile loaded next
@@ -699,18 +699,22 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
     if (t + 2 < ntiles) load_tile(t + 2, nb0, nb1);
     const int kt0 = t * kKeys;
     if (kt0 < wkend) {
-      const char *slot = ring_bytes + (t % kRing) * kSlot;
+      // The tile's K and V^T read addresses, one register each; the empty asm
+      // keeps the compiler from folding the slot into per-read constants and
+      // hoisting those out of the loop (16 registers, and two adds per read),
+      // so every read below is the register plus an immediate offset.
+      const uint32_t slot = ring0 + (uint32_t)(t % kRing) * kSlot;
+      uint32_t ka = slot + k_lane, va = slot + kSlotK + v_lane;
+      asm("" : "+v"(ka), "+v"(va));
       // half the V^T operands read before the softmax (measured on MI355X:
       // 1-1.5% faster on whole prompts, 0.6% on chunks; all of them do not
       // fit three workgroups per CU)
       attend_tile<D, OB / 2>(
-          [&](int hh, int i) {
-            return *reinterpret_cast<const bf16x8_t *>(slot + k_lane + hh * 4 * kGrp + i * 256);
-          },
+          [&](int hh, int i) { return *(const lds_bf16x8_t *)(uintptr_t)(ka + hh * 4 * kGrp + i * 256); },
           [&](int j) {
-            const char *v = slot + kSlotK + v_lane + (j >> 1) * 256 + (j & 1) * 32;
-            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)v);
-            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(v + 4 * kGrp));
+            const uint32_t v = va + (j >> 1) * 256 + (j & 1) * 32;
+            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)v);
+            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(uintptr_t)(v + 4 * kGrp));
             return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           },
           rows.qop, o, m, l, rows.prow, kt0, first_pos + tok0, g, a.qscale, xor16, xor32);
