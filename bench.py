@@ -346,6 +346,13 @@ def causal_flops(context_lens, cu_seqlens, num_q_heads, head_dim):
     return pairs * num_q_heads * 4 * head_dim
 
 
+def prefill_kernel_name(head_dim, block_size):
+    """The pa_prefill kernel that serves a shape: tiles loaded straight into
+    LDS for head_dim 128 at block sizes of 8 and up, staged through
+    registers otherwise."""
+    return "prefill_ring_kernel" if head_dim == 128 and block_size >= 8 else "prefill_kernel"
+
+
 def prefill_flops(pc):
     return causal_flops(pc.case.context_lens, pc.cu_seqlens, pc.case.num_q_heads, pc.case.head_dim)
 
@@ -449,7 +456,7 @@ def prefill_main(args, torch, pkv, dev):
         "write_bytes_per_step": write_bytes,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel", "avg_launch_us": round(avg * 1e6, 2),
+                     "kernel": prefill_kernel_name(c.head_dim, c.block_size), "avg_launch_us": round(avg * 1e6, 2),
                      "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None,
     }
@@ -712,7 +719,7 @@ def prefix_main(args, torch, pkv, dev):
         "speedup_vs_uncached": round(step_u / step_s, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel", "avg_launch_us": round(prefill_s * 1e6, 2),
+                     "kernel": prefill_kernel_name(plan.head_dim, bs), "avg_launch_us": round(prefill_s * 1e6, 2),
                      "algorithmic_flops_per_launch": flops,
                      "uncached_avg_launch_us": round(prefill_u * 1e6, 2)},
         "cpu_baseline": None,
