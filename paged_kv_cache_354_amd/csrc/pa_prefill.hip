@@ -67,6 +67,7 @@ constexpr int kRB = 2;         // 16-row blocks per wave
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr int kRankSeqs = 32; // batches up to this many sequences run longest first
 constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
+constexpr float kLazyW = 256.0f;   // 2^kLazyMax
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
 constexpr int kWaitVmem = 0x0F70;
 
@@ -245,19 +246,26 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
         for (int e = 0; e < 4; ++e)
           if (16 * hh + e > lim) z[4 * hh + e] = -INFINITY;
     }
-    // maximum (NaN-propagating) takes matrix-core results as they are;
-    // fmaxf would first quiet each of them, one more instruction each
-    float mx = z[0];
+    // Weights against the current reference max m.  m moves only when some
+    // weight comes out above 2^kLazyMax (a score passed m by more than
+    // kLazyMax, log2 units; +inf included, NaN not: a NaN score stays NaN
+    // either way): then the row max over its 4 lanes becomes m and the
+    // weights are recomputed.  So the rescale of O^T is rare after the first
+    // tiles, and the common path spends no instruction on the max's scale
+    // or the threshold.  The result does not depend on m.
+    f32x8_t p;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
-    mx *= qscale;
-    // The reference max m moves only when some score passes it by more
-    // than kLazyMax (log2 units): the weights 2^(z - m) then stay below
-    // 2^kLazyMax, and the rescale of O^T is rare after the first tiles.
-    // The test needs only this lane's max; inside, every row takes the
-    // max over its 4 lanes, so the 4 lanes of a row keep one m.  The
-    // result does not depend on m.
-    if (__any(mx > m[rb] + kLazyMax)) {
+    for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], qscale, -m[rb]));
+    // maximum (NaN-propagating) takes the weights as they are; fmaxf would
+    // first quiet each of them, one more instruction each
+    float pmax = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) pmax = __builtin_elementwise_maximum(pmax, p[e]);
+    if (__any(pmax > kLazyW)) {
+      float mx = z[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
+      mx *= qscale;
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor16, __float_as_int(mx))));
       mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(xor32, __float_as_int(mx))));
       const float mn = fmaxf(m[rb], mx);
@@ -266,11 +274,9 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
       l[rb] *= alpha;
 #pragma unroll
       for (int j = 0; j < OB; ++j) o[rb][j] *= alpha;
-    }
-    f32x8_t p;
-    const float negm = -m[rb];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], qscale, negm));
+      for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], qscale, -mn));
+    }
     float ps = p[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) ps += p[e];
