@@ -209,16 +209,16 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
         st[rb][hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], __builtin_bit_cast(bf16x8_t, qop[rb][i]),
                                                              st[rb][hh], 0, 0, 0);
   }
-  // Two waves share each SIMD: a wave in its softmax (a chain of vector
-  // instructions) runs at a higher priority than one issuing matrix ops,
-  // so it gets through and reaches its own matrix ops sooner while the
-  // other's are in the pipeline (measured on MI355X: 1.3-1.5% faster;
-  // the opposite, or raising it already at the V^T reads, was not).
   // V^T operands read now, into the registers the K operands held, arrive
   // during the softmax.
   bf16x8_t vop_early[VEARLY > 0 ? VEARLY : 1];
 #pragma unroll
   for (int j = 0; j < VEARLY; ++j) vop_early[j] = vop_at(j);
+  // Waves share each SIMD: a wave in its softmax (a chain of vector
+  // instructions) runs at a higher priority than one issuing matrix ops,
+  // so it gets through and reaches its own matrix ops sooner while the
+  // other's are in the pipeline (measured on MI355X: 1.3-1.5% faster;
+  // the opposite, or raising it already at the V^T reads, was not).
   __builtin_amdgcn_s_setprio(2);
   // Per row block: causal mask (only where the tile reaches past the
   // block's first row), reference max, probabilities.
