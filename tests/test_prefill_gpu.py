@@ -70,9 +70,14 @@ def out_to_f64_np(a):
     return np.where(np.isfinite(finite), finite, 0.0)
 
 
+# head_dim 128 at block sizes 8..256 runs the kernel that loads tiles
+# straight into LDS (groups of 4 keys must not straddle a block: 8 is the
+# smallest size it takes); head_dim 64, and head_dim 128 below block size
+# 8, run the register-staged kernel.
 @pytest.mark.parametrize("hq,hkv,d,bs", [(32, 8, 128, 16), (64, 8, 128, 16), (16, 8, 128, 32),
-                                         (8, 8, 128, 16), (16, 4, 64, 8), (32, 8, 64, 1), (16, 8, 64, 16),
-                                         (64, 8, 64, 32)])
+                                         (8, 8, 128, 16), (32, 8, 128, 8), (32, 8, 128, 64), (16, 8, 128, 256),
+                                         (32, 8, 128, 4), (32, 8, 128, 1), (16, 4, 64, 8), (32, 8, 64, 1),
+                                         (16, 8, 64, 16), (64, 8, 64, 32)])
 def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
     rng = np.random.default_rng(hq + d + bs)
     lens = [1, 15, 16, 17, 100, 333, 64, 40]
