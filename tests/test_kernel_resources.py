@@ -12,7 +12,9 @@ here (an ELF note per code object) and check:
 
 - no kernel uses scratch (private segment) or spills VGPRs;
 - those kernels keep three workgroups per CU at the Llama-3-8B shape
-  (head_dim 128, four query heads per KV head).
+  (head_dim 128, four query heads per KV head);
+- M0, which the LDS-loading prefill kernel sets from inline assembly, is
+  used by nothing else (read from the disassembly of the same code objects).
 """
 
 import os
@@ -36,9 +38,10 @@ def _tool(name):
 
 
 @pytest.fixture(scope="module")
-def kernels(tmp_path_factory):
-    objcopy, readelf = _tool("llvm-objcopy"), _tool("llvm-readelf")
-    if not os.path.exists(LIB) or not objcopy or not readelf:
+def code_objects(tmp_path_factory):
+    """The gfx950 code objects of the built library (one per HIP source)."""
+    objcopy = _tool("llvm-objcopy")
+    if not os.path.exists(LIB) or not objcopy or not _tool("llvm-readelf") or not _tool("llvm-objdump"):
         pytest.skip("libpagedkv.so or the LLVM binary tools are not available")
     tmp = tmp_path_factory.mktemp("code_objects")
     fat = tmp / "fatbin"
@@ -46,7 +49,7 @@ def kernels(tmp_path_factory):
     data = fat.read_bytes()
     # offload bundles, one per HIP source: magic, entry count, then
     # (offset, size, triple length, triple) per entry, offsets from the magic
-    meta = {}
+    paths = []
     start = data.find(BUNDLE_MAGIC)
     while start >= 0:
         (count,) = struct.unpack_from("<Q", data, start + len(BUNDLE_MAGIC))
@@ -59,13 +62,38 @@ def kernels(tmp_path_factory):
                 continue
             co = tmp / f"co_{start}.elf"
             co.write_bytes(data[start + off:start + off + size])
-            notes = subprocess.run([readelf, "--notes", str(co)], check=True, capture_output=True, text=True).stdout
-            doc = yaml.safe_load(notes[notes.index("---"):notes.rindex("...")])
-            for k in doc["amdhsa.kernels"]:
-                meta[k[".name"]] = k
+            paths.append(co)
         start = data.find(BUNDLE_MAGIC, start + 1)
-    assert meta, "no gfx950 code objects in libpagedkv.so"
+    assert paths, "no gfx950 code objects in libpagedkv.so"
+    return paths
+
+
+@pytest.fixture(scope="module")
+def kernels(code_objects):
+    meta = {}
+    for co in code_objects:
+        notes = subprocess.run([_tool("llvm-readelf"), "--notes", str(co)], check=True, capture_output=True,
+                               text=True).stdout
+        doc = yaml.safe_load(notes[notes.index("---"):notes.rindex("...")])
+        for k in doc["amdhsa.kernels"]:
+            meta[k[".name"]] = k
     return meta
+
+
+def disassembly(code_objects):
+    """{kernel symbol: [instruction text, ...]} of every kernel built here."""
+    out = {}
+    for co in code_objects:
+        text = subprocess.run([_tool("llvm-objdump"), "-d", "--mcpu=gfx950", str(co)], check=True,
+                              capture_output=True, text=True).stdout
+        cur = None
+        for line in text.splitlines():
+            if line.endswith(">:"):
+                cur = line[line.index("<") + 1:-2]
+                out[cur] = []
+            elif cur and line.startswith("\t"):
+                out[cur].append(line.strip().split("//")[0].strip())
+    return out
 
 
 def _find(kernels, *parts):
@@ -116,3 +144,31 @@ def test_occupancy_model_reads_metadata_as_expected():
     assert workgroups_per_cu({".vgpr_count": 168, ".group_segment_fixed_size": 1024}) == 3
     assert workgroups_per_cu({".vgpr_count": 169, ".group_segment_fixed_size": 1024}) == 2
     assert workgroups_per_cu({".vgpr_count": 64, ".group_segment_fixed_size": 60 * 1024}) == 2
+
+
+# instructions that read M0 without naming it
+IMPLICIT_M0 = ("s_sendmsg", "v_movrel", "s_movrel", "ds_gws", "_addtid", "v_interp", "s_ttracedata", "buffer_load_lds",
+               "global_load_lds", "buffer_store_lds")
+
+
+def test_m0_is_written_only_for_the_lds_loads(code_objects):
+    """The prefill kernel that loads tiles straight into LDS sets M0 (the
+    LDS address of those loads) from inline assembly, which clang allows but
+    does not track.  That is sound only while nothing else in the kernels
+    uses M0: every M0 write must be ours (s_mov_b32 m0, sN; s_nop 0;
+    global_load_lds_dwordx4), and no other instruction may read it."""
+    dis = disassembly(code_objects)
+    ring = [n for n in dis if "prefill_ring_kernel" in n]
+    assert ring, "no prefill_ring_kernel in the library"
+    for name, ins in dis.items():
+        for i, text in enumerate(ins):
+            op = text.split()[0] if text else ""
+            names_m0 = any(t.strip(",") == "m0" for t in text.split()[1:])
+            if names_m0:
+                assert name in ring and op == "s_mov_b32" and ins[i + 1] == "s_nop 0" and \
+                    ins[i + 2].startswith("global_load_lds_dwordx4"), f"{name}: M0 use at '{text}'"
+            if any(k in op for k in IMPLICIT_M0):
+                assert name in ring and op == "global_load_lds_dwordx4" and ins[i - 2].startswith("s_mov_b32 m0,"), \
+                    f"{name}: '{text}' reads M0"
+    # and the loads are there: 4 per tile-load site
+    assert all(sum(t.startswith("global_load_lds_dwordx4") for t in dis[n]) >= 4 for n in ring)
