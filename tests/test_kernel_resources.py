@@ -172,3 +172,20 @@ def test_m0_is_written_only_for_the_lds_loads(code_objects):
                     f"{name}: '{text}' reads M0"
     # and the loads are there: 4 per tile-load site
     assert all(sum(t.startswith("global_load_lds_dwordx4") for t in dis[n]) >= 4 for n in ring)
+
+
+def test_ring_kernel_tile_loads_are_the_only_vector_loads_in_flight(code_objects):
+    """The LDS-loading prefill kernel waits on its tile loads with explicit
+    vmcnt counts, which hold only while no vector load the compiler issued
+    is outstanding in the tile loop: in program order every other vector
+    load (queries, lengths, offsets) comes before the first tile load, and
+    the block ids are scalar loads."""
+    dis = disassembly(code_objects)
+    for name, ins in dis.items():
+        if "prefill_ring_kernel" not in name:
+            continue
+        first = next(i for i, t in enumerate(ins) if t.startswith("global_load_lds_dwordx4"))
+        late = [t for t in ins[first:] if t.startswith(("global_load", "buffer_load", "flat_load", "scratch_load"))
+                and not t.startswith("global_load_lds_dwordx4")]
+        assert not late, f"{name}: vector loads after the first tile load: {late[:3]}"
+        assert any(t.startswith("s_load_dword ") for t in ins[first:]), f"{name}: block ids not scalar loads"
