@@ -136,7 +136,8 @@ def parse_args(argv=None):
                    help="KV pool copies that consecutive steps rotate over (1: same pool every step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--separate-write", action="store_true",
-                   help="pa_write_kv then pa_decode instead of one pa_decode_write call")
+                   help="pa_write_kv then pa_decode (or pa_prefill) instead of one pa_decode_write "
+                        "(pa_prefill_write) call")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline time budget")
     p.add_argument("--block-size", type=int, default=16,
                    help="waste workloads: tokens per KV block of the paged run (the block-size knob)")
@@ -390,7 +391,9 @@ def prefill_cpu_baseline(pc, budget_s):
 
 
 def prefill_main(args, torch, pkv, dev):
-    """One step: pa_write_kv of the chunk's tokens, then pa_prefill."""
+    """One step: the chunk's tokens stored and their queries attended, as one
+    pa_prefill_write call (or pa_write_kv, then pa_prefill, with
+    --separate-write)."""
     log(f"workload {args.workload}: drawing inputs")
     pc = PREFILL_WORKLOADS[args.workload]()
     c = pc.case
@@ -406,11 +409,16 @@ def prefill_main(args, torch, pkv, dev):
     q, kn, vn, slots = dev_t(pc.q), dev_t(pc.k_new), dev_t(pc.v_new), dev_t(pc.slot_mapping)
     tables, lens, cu = dev_t(c.block_tables), dev_t(c.context_lens), dev_t(pc.cu_seqlens)
     out = torch.empty_like(q)
+    fused = not args.separate_write
     steps = []
     for kc, vc in layers:
-        steps.append((pkv.prepare_write_kv(kn, vn, slots, kc, vc),
-                      pkv.prepare_prefill(q, kc, vc, tables, lens, cu, pc.max_query_len, c.max_context, c.scale,
-                                          out)))
+        if fused:
+            steps.append((pkv.prepare_prefill_write(kn, vn, slots, q, kc, vc, tables, lens, cu, pc.max_query_len,
+                                                    c.max_context, c.scale, out),))
+        else:
+            steps.append((pkv.prepare_write_kv(kn, vn, slots, kc, vc),
+                          pkv.prepare_prefill(q, kc, vc, tables, lens, cu, pc.max_query_len, c.max_context,
+                                              c.scale, out)))
     torch.cuda.synchronize()
     for i in range(args.warmup):
         for call in steps[i % len(steps)]:
@@ -426,7 +434,7 @@ def prefill_main(args, torch, pkv, dev):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(args.steps):
-        steps[i % len(steps)][1]()
+        steps[i % len(steps)][-1]()  # the attention call (with the store when fused)
     e1.record()
     torch.cuda.synchronize()
     avg = e0.elapsed_time(e1) / 1e3 / args.steps
@@ -450,7 +458,8 @@ def prefill_main(args, torch, pkv, dev):
         "config": {"workload": args.workload, "num_seqs": c.num_seqs, "num_q_heads": c.num_q_heads,
                    "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "block_size": c.block_size,
                    "query_tokens": pc.num_tokens, "context_len_mean": round(float(c.context_lens.mean()), 1),
-                   "context_len_max": int(c.context_lens.max()), "kv_pool_copies": len(layers)},
+                   "context_len_max": int(c.context_lens.max()), "kv_pool_copies": len(layers),
+                   "write_fused_into_prefill": fused},
         "pct_of_peak": round(100.0 * flops / (wall / args.steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
         "flops_per_step": flops,
         "write_bytes_per_step": write_bytes,
@@ -649,9 +658,17 @@ def prefix_main(args, torch, pkv, dev):
     q, kn, vn = dev_t(plan.suffix_q), dev_t(plan.suffix_k), dev_t(plan.suffix_v)
     out = torch.empty_like(q)
     max_q = int(plan.suffix_lens.max())
-    steps = [(pkv.prepare_write_kv(kn, vn, slots, kc, vc),
-              pkv.prepare_prefill(q, kc, vc, tables, ctx_d, cu, max_q, int(lens.max()), plan.scale, out))
-             for slots, tables in plans]
+    fused = not args.separate_write
+
+    def store_and_attend(k, v, slots, q_, tables, cu_, max_q_, out_):
+        # the step's store and attention: one pa_prefill_write call, or the two calls
+        if fused:
+            return (pkv.prepare_prefill_write(k, v, slots, q_, kc, vc, tables, ctx_d, cu_, max_q_, int(lens.max()),
+                                              plan.scale, out_),)
+        return (pkv.prepare_write_kv(k, v, slots, kc, vc),
+                pkv.prepare_prefill(q_, kc, vc, tables, ctx_d, cu_, max_q_, int(lens.max()), plan.scale, out_))
+
+    steps = [store_and_attend(kn, vn, slots, q, tables, cu, max_q, out) for slots, tables in plans]
 
     def timed(calls, kernel_index):
         torch.cuda.synchronize()
@@ -674,7 +691,7 @@ def prefix_main(args, torch, pkv, dev):
         return wall / args.steps, e0.elapsed_time(e1) / 1e3 / args.steps
 
     log(f"timed {args.steps} cached steps")
-    step_s, prefill_s = timed(steps, 1)
+    step_s, prefill_s = timed(steps, -1)
 
     log("uncached comparison: every prompt stored and prefilled whole")
     pool_u = pkv.BlockPool(plan.num_blocks, bs, plan.free_order)
@@ -690,10 +707,8 @@ def prefix_main(args, torch, pkv, dev):
     kf = torch.cat([x for s in range(B) for x in (kp, kn[suf_cu[s]:suf_cu[s + 1]])])
     vf = torch.cat([x for s in range(B) for x in (vp, vn[suf_cu[s]:suf_cu[s + 1]])])
     out_f = torch.empty_like(qf)
-    steps_u = [(pkv.prepare_write_kv(kf, vf, dev_t(slots_u), kc, vc),
-                pkv.prepare_prefill(qf, kc, vc, dev_t(tab_u), ctx_d, dev_t(cu_full), int(lens.max()),
-                                    int(lens.max()), plan.scale, out_f))]
-    step_u, prefill_u = timed(steps_u, 1)
+    steps_u = [store_and_attend(kf, vf, dev_t(slots_u), qf, dev_t(tab_u), dev_t(cu_full), int(lens.max()), out_f)]
+    step_u, prefill_u = timed(steps_u, -1)
 
     prompt_tokens = int(lens.sum())
     computed = int(plan.suffix_lens.sum())
@@ -711,7 +726,7 @@ def prefix_main(args, torch, pkv, dev):
                    "suffix_tokens_min": int(plan.suffix_lens.min()), "suffix_tokens_max": int(plan.suffix_lens.max()),
                    "prompt_tokens_per_step": prompt_tokens, "computed_tokens_per_step": computed,
                    "num_q_heads": plan.num_q_heads, "num_kv_heads": plan.num_kv_heads,
-                   "head_dim": plan.head_dim, "block_size": bs},
+                   "head_dim": plan.head_dim, "block_size": bs, "write_fused_into_prefill": fused},
         "cache_hit_fraction": round(cached_tokens / (nsteps * prompt_tokens), 4),
         "host_manager_us_per_request": round(host_s / (nsteps * B) * 1e6, 2),
         "uncached_tokens_per_s": round(prompt_tokens / step_u, 1),

@@ -298,6 +298,38 @@ pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num_q_heads,
                        void *out, int32_t out_dtype, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_prefill_write -- pa_write_kv(k, v, slot_mapping, num_tokens) followed by
+ * pa_prefill(...), as one call: a prompt's (or chunk's) keys and values are
+ * stored in their blocks and its queries attend.
+ * (foundry PagedAttention page, "How it works": new tokens' keys and values
+ * go into the sequence's blocks, and attention reads the whole context, the
+ * new tokens included, through the block table; a prompt is many tokens.)
+ *
+ * Arguments: k, v (device [num_tokens][num_kv_heads][head_dim], bf16: row r
+ * holds the key and value of query row r) and slot_mapping (device int64
+ * [num_tokens]; slots < 0 or outside the pool are skipped), then those of
+ * pa_prefill; k_cache and v_cache are written.  The pools after the call and
+ * out are those of the two calls in sequence (bitwise), given this
+ * precondition: cu_seqlens[num_seqs] == num_tokens, no length above
+ * min(max_context_len, max_blocks_per_seq * block_size), and for every row r
+ * of sequence s, slot_mapping[r] is the slot the block table gives for the
+ * row's position context_lens[s] - n_s + (r - cu_seqlens[s]) (or < 0 only
+ * where that position is below 0).  With head_dim 128 and block_size >= 8
+ * that is one kernel: the rows are stored while it runs and the attention
+ * reads the chunk's keys and values from k and v themselves.  Otherwise the
+ * call runs pa_write_kv, then pa_prefill.  Errors: those of the two calls,
+ * all found before anything is enqueued, plus PA_EINVAL when k or v is not
+ * 16-byte aligned; num_seqs, max_query_len == 0: only the store is done.
+ * ------------------------------------------------------------------------ */
+pa_status_t pa_prefill_write(const void *k, const void *v, const int64_t *slot_mapping, const void *q,
+                             int32_t num_tokens, int32_t num_q_heads, const int32_t *cu_seqlens,
+                             int32_t num_seqs, int32_t max_query_len, void *k_cache, void *v_cache,
+                             const pa_cache_t *cache, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *context_lens,
+                             int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                             void *stream);
+
+/* ---------------------------------------------------------------------------
  * Host block manager (host memory only, no device calls).
  * (foundry PagedAttention page, "Concept", "How it works", "At a glance";
  * aiacademy lesson "Paged Attention", analogy table.)

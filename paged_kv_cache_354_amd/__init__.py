@@ -16,6 +16,8 @@ The functions carry the C names declared in ``include/pa.h``:
 * ``pa_decode_write_noalloc`` -- the same without a workspace, for callers
   that cannot allocate (a static scratch array in the library serves)
 * ``pa_prefill``      -- causal paged attention of a chunk of new queries
+* ``pa_prefill_write`` -- ``pa_write_kv`` of the chunk's keys and values, then
+  ``pa_prefill``, in one call
 * ``pa_decode_workspace_bytes``
 * ``pa_pool_*`` / ``pa_seq_*`` -- host block manager (free pool, reference
   counts, block tables, copy-on-write decisions)
@@ -91,6 +93,8 @@ _SIGS = {
                                        _vp, _i32, _vp, _i32, ctypes.c_float, _i32, _vp, _i32, _vp]),
     "pa_prefill": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache), _vp, _i32, _vp,
                           _i32, ctypes.c_float, _vp, _i32, _vp]),
+    "pa_prefill_write": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, ctypes.POINTER(PaCache),
+                                _vp, _i32, _vp, _i32, ctypes.c_float, _vp, _i32, _vp]),
     "pa_pool_create": (_i32, [_i32, _i32, _P32, ctypes.POINTER(_vp)]),
     "pa_pool_destroy": (None, [_vp]),
     "pa_pool_num_free": (_i32, [_vp]),
@@ -423,6 +427,42 @@ def prepare_prefill(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens,
     args, _, keep = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
                                   max_context_len, scale, out, None, stream)
     fn = load().pa_prefill
+
+    def call():
+        _check(fn(*args))
+    call.keep = keep
+    return call
+
+
+def _prefill_write_args(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, cu_seqlens,
+                        max_query_len, max_context_len, scale, out, out_dtype, stream):
+    args, out, keep = _prefill_args(q, k_cache, v_cache, block_tables, context_lens, cu_seqlens, max_query_len,
+                                    max_context_len, scale, out, out_dtype, stream)
+    nt = _new_token_args(k, v, slot_mapping, k_cache)
+    if nt[3] != args[1]:
+        raise ValueError("k, v and slot_mapping must have one row per query row")
+    return nt[:3] + args, out, keep + (k, v, slot_mapping)
+
+
+def pa_prefill_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, cu_seqlens,
+                     max_query_len, max_context_len, scale, out=None, out_dtype=None, stream=None):
+    """``pa_write_kv(k, v, slot_mapping)`` then ``pa_prefill`` as one call
+    (one kernel for head_dim 128 and block sizes of 8 and up): row r of
+    ``k``/``v`` ``[T][Hkv][d]`` is the key and value of query row r, stored at
+    ``slot_mapping[r]``; returns ``out``."""
+    args, out, _ = _prefill_write_args(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                                       cu_seqlens, max_query_len, max_context_len, scale, out, out_dtype, stream)
+    _check(load().pa_prefill_write(*args))
+    return out
+
+
+def prepare_prefill_write(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens, cu_seqlens,
+                          max_query_len, max_context_len, scale, out, stream=None):
+    """``pa_prefill_write`` with its arguments checked once; ``out`` must be
+    given."""
+    args, _, keep = _prefill_write_args(k, v, slot_mapping, q, k_cache, v_cache, block_tables, context_lens,
+                                        cu_seqlens, max_query_len, max_context_len, scale, out, None, stream)
+    fn = load().pa_prefill_write
 
     def call():
         _check(fn(*args))

@@ -66,8 +66,7 @@ constexpr int kKeys = 32;      // keys per tile
 constexpr int kRB = 2;         // 16-row blocks per wave
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr int kRankSeqs = 32; // batches up to this many sequences run longest first
-constexpr float kLazyMax = 8.0f;  // headroom of the running max, log2 units (weights <= 256)
-constexpr float kLazyW = 256.0f;   // 2^kLazyMax
+constexpr float kLazyW = 256.0f;  // headroom of the running max: weights up to 2^8 (8 in log2 units)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
 constexpr int kWaitVmem = 0x0F70;
 
@@ -90,6 +89,13 @@ struct PrefillArgs {
   int32_t q_blocks;  // query blocks (of the workgroup's tokens) per sequence in the grid
   int32_t out_f32;   // 1: fp32 output, 0: bf16
   float qscale;      // scale * log2(e)
+  // Fused store (pa_prefill_write; k_new NULL otherwise): query row r's key
+  // and value rows, [T][Hkv][D], go to pool slot slot_mapping[r], and the
+  // attention reads the chunk's keys from these rows.
+  const uint4 *k_new;
+  const uint4 *v_new;
+  const int64_t *slot_mapping;
+  int64_t num_slots;  // num_blocks * block_size
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -247,8 +253,8 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
           if (16 * hh + e > lim) z[4 * hh + e] = -INFINITY;
     }
     // Weights against the current reference max m.  m moves only when some
-    // weight comes out above 2^kLazyMax (a score passed m by more than
-    // kLazyMax, log2 units; +inf included, NaN not: a NaN score stays NaN
+    // weight comes out above kLazyW = 2^8 (a score passed m by more than 8,
+    // log2 units; +inf included, NaN not: a NaN score stays NaN
     // either way): then the row max over its 4 lanes becomes m and the
     // weights are recomputed.  So the rescale of O^T is rare after the first
     // tiles, and the common path spends no instruction on the max's scale
@@ -578,11 +584,15 @@ typedef __attribute__((address_space(4))) const int32_t const_i32;
 // the LDS address (the compiler uses M0 for nothing in these kernels; it is
 // declared clobbered all the same, which clang notes as a reserved register).
 // One wait state between the M0 write and the load that reads it.
+// load_lds16_at: the same from a 64-bit address per lane.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void load_lds16(uint64_t base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
                : "m0");
+}
+__device__ __forceinline__ void load_lds16_at(uint64_t addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr) : "m0");
 }
 #pragma clang diagnostic pop
 
@@ -591,7 +601,12 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32);
 }
 
-template <int G>
+// WRITE: the fused store of pa_prefill_write.  The workgroups of head group
+// 0 store their query tokens' key and value rows of their KV head (so every
+// new row is stored once), and every workgroup reads the chunk's keys (its
+// last n positions) from those input rows, not from the pools: no workgroup
+// waits for another's stores.
+template <int G, bool WRITE>
 // Three workgroups per CU: 3 x 50,688 bytes of ring fit the 160 KiB of LDS.
 __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a) {
   constexpr int D = 128;
@@ -620,8 +635,65 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   const int kend = max(0, min(ctx, first_pos + min(q0 + TQ, n)));
   const int wkend = tok0 < n ? max(0, min(ctx, first_pos + min(tok0 + 16 * kRB, n))) : 0;
 
+  // WRITE, head group 0: rows q0 .. q0 + TQ - 1 of the chunk (those that
+  // exist), KV head kvh, 16 bytes of K and of V per item.
+  // - 32 tokens per workgroup (4 or 8 query heads per KV head): the rows
+  //   are the workgroup's last keys, so after the tile loop they sit in the
+  //   last two ring slots (brought from the input rows); they are stored from
+  //   there, and only their slots are loaded up front.  No wait covers these
+  //   stores (measured on MI355X: the stores and row loads at the start cost
+  //   ~19 us per call on whole prompts).
+  // - more tokens per workgroup: the rows are loaded with the queries (one
+  //   round trip for both) and stored just before the first tile loads;
+  //   vmcnt counts stores too, in issue order, so the tile loop's first wait
+  //   covers them along with the first tile's loads, and no later wait does.
+  constexpr bool kStoreFromLds = TQ == kKeys;
+  constexpr int kStoreItems = TQ * (D / 8);
+  constexpr int NST = WRITE ? (kStoreItems + kThreads - 1) / kThreads : 1;
+  const bool storing = WRITE && wk.hg == 0;
+  const int items = storing ? min(TQ, n - q0) * (D / 8) : 0;
+  // a vector type, not uint4: a uint4 copied from memory becomes a memcpy
+  // that leaves these arrays on the stack
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t st_k[NST], st_v[NST];
+  int64_t st_slot[NST];
+  if constexpr (WRITE) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int i = tid + j * kThreads;
+      st_slot[j] = -1;
+      if (i < items) {
+        const int r = lo + q0 + i / (D / 8);
+        const size_t src = ((size_t)r * a.num_kv_heads + kvh) * (D / 8) + i % (D / 8);
+        st_slot[j] = a.slot_mapping[r];
+        if constexpr (!kStoreFromLds) {
+          st_k[j] = reinterpret_cast<const u32x4_t *>(a.k_new)[src];
+          st_v[j] = reinterpret_cast<const u32x4_t *>(a.v_new)[src];
+        }
+      }
+    }
+  }
+
   WaveRows<D> rows;
   rows.load(a, lo, n, first_pos, tok0, h, nl, g);
+
+  // The query rows (and the rows to store) have arrived before any tile
+  // load is issued: from here on, vmcnt counts the stores and then this
+  // wave's tile loads only.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  if constexpr (WRITE && !kStoreFromLds) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int i = tid + j * kThreads;
+      const int64_t slot = st_slot[j];
+      if (i < items && slot >= 0 && slot < a.num_slots) {  // slots < 0 or outside the pool are skipped
+        const size_t dst = (((size_t)(slot >> a.log2_bs) * a.num_kv_heads + kvh) * a.block_size +
+                            (slot & (a.block_size - 1))) * (D / 8) + i % (D / 8);
+        reinterpret_cast<u32x4_t *>(const_cast<uint4 *>(a.k_cache))[dst] = st_k[j];
+        reinterpret_cast<u32x4_t *>(const_cast<uint4 *>(a.v_cache))[dst] = st_v[j];
+      }
+    }
+  }
 
   f32x4_t o[kRB][OB];  // O^T: channel 16j + 4g + e of row nl of block rb
 #pragma unroll
@@ -634,9 +706,6 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
     m[rb] = kNegBig;
     l[rb] = 0.0f;
   }
-  // The query rows have arrived before any tile load is issued: from here
-  // on, vmcnt counts this wave's tile loads only.
-  __builtin_amdgcn_s_waitcnt(kWaitVmem);
 
   const_i32 *trow = (const_i32 *)(a.block_tables + (size_t)s * a.max_blocks);
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
@@ -644,8 +713,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   const uint64_t head_bytes = (uint64_t)kvh * a.block_size * kRowBytes;
   const uint64_t kbase = (uint64_t)(uintptr_t)a.k_cache + head_bytes;
   const uint64_t vbase = (uint64_t)(uintptr_t)a.v_cache + head_bytes;
-  const uint32_t lane_off = ((lane >> 2) & 3) * kRowBytes + (lane >> 4) * 64 + (lane & 3) * 16;
+  const uint32_t lane_seg = (lane >> 4) * 64 + (lane & 3) * 16;  // segment and chunk of the lane's 16 bytes
+  const uint32_t lane_off = ((lane >> 2) & 3) * kRowBytes + lane_seg;
   const int bmask = a.block_size - 1;
+  // the chunk's rows (WRITE): position p >= first_pos is row lo + p - first_pos
+  const uint32_t new_row_bytes = (uint32_t)a.num_kv_heads * kRowBytes;
+  const uint64_t knew = (uint64_t)(uintptr_t)a.k_new + (uint64_t)kvh * kRowBytes;
+  const uint64_t vnew = (uint64_t)(uintptr_t)a.v_new + (uint64_t)kvh * kRowBytes;
+  auto new_row_at = [&](int p) -> uint64_t { return (uint64_t)(uint32_t)(lo + p - first_pos) * new_row_bytes; };
 
   // The table entry of group grp (keys 32u + 8 wave + 4 grp ..) of tile u.
   // A group's 4 keys share a block (block size >= 8, groups 4-aligned).
@@ -664,6 +739,26 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
     for (int grp = 0; grp < 2; ++grp) {
       const int qg = 2 * wave + grp;
       const int kt = u * kKeys + 4 * qg;
+      if (WRITE && min(kt + 3, kend - 1) >= first_pos) {  // uniform: the group holds keys of the chunk
+        const uint32_t kdst = __builtin_amdgcn_readfirstlane(slot + qg * kGrp);
+        const uint32_t vdst = __builtin_amdgcn_readfirstlane(slot + kSlotK + qg * kGrp);
+        const int p = min(kt + ((lane >> 2) & 3), kend - 1);  // the lane's key
+        if (kt >= first_pos) {  // all from the chunk's rows
+          const int key0 = min(kt, kend - 1);
+          const uint32_t voff = (uint32_t)(p - key0) * new_row_bytes + lane_seg;
+          load_lds16(uniform64(knew + new_row_at(key0)), voff, kdst);
+          load_lds16(uniform64(vnew + new_row_at(key0)), voff, vdst);
+        } else {  // keys before first_pos from the pool (block of kt), the rest from the chunk's rows
+          const int blk = grp ? blk1 : blk0;
+          const uint32_t pb = (unsigned)blk < (unsigned)a.num_blocks ? (uint32_t)blk : 0u;
+          const uint64_t pool = (uint64_t)pb * block_bytes + (uint64_t)(p & bmask) * kRowBytes + lane_seg;
+          const bool fresh = p >= first_pos;
+          const uint64_t nrow = fresh ? new_row_at(p) + lane_seg : 0;
+          load_lds16_at(fresh ? knew + nrow : kbase + pool, kdst);
+          load_lds16_at(fresh ? vnew + nrow : vbase + pool, vdst);
+        }
+        continue;
+      }
       int key0 = kt;
       uint32_t voff = lane_off;
       if (kt + 3 >= kend) {  // uniform: the group reaches kend
@@ -733,15 +828,43 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       nb1 = block_of(t + 3, 1);
     }
   }
+  if constexpr (WRITE && kStoreFromLds) {
+    // Row i of the workgroup's tokens (position first_pos + q0 + i) is key
+    // p of tile p / 32, in ring slot (p / 32) % 3: group (p % 32) / 4, row
+    // p % 4 of it, segment c / 4, chunk c % 4 (c the 16-byte chunk).  The
+    // last two tiles hold all of them, and no tile load came after them.
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int i = tid + j * kThreads;
+      const int64_t slot = st_slot[j];
+      const int p = first_pos + q0 + i / (D / 8), c = i % (D / 8);
+      // slots < 0 or outside the pool are skipped, and so are positions
+      // below 0 (which no tile holds; their slots are < 0)
+      if (i < items && p >= 0 && slot >= 0 && slot < a.num_slots) {
+        const uint32_t at = (uint32_t)((p / kKeys) % kRing) * kSlot + ((p % kKeys) >> 2) * kGrp + (c >> 2) * 256 +
+                            (p & 3) * 64 + (c & 3) * 16;
+        const u32x4_t kv = *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)(ring0 + at);
+        const u32x4_t vv = *(const __attribute__((address_space(3))) u32x4_t *)(uintptr_t)(ring0 + at + kSlotK);
+        const size_t dst = (((size_t)(slot >> a.log2_bs) * a.num_kv_heads + kvh) * a.block_size +
+                            (slot & (a.block_size - 1))) * (D / 8) + c;
+        reinterpret_cast<u32x4_t *>(const_cast<uint4 *>(a.k_cache))[dst] = kv;
+        reinterpret_cast<u32x4_t *>(const_cast<uint4 *>(a.v_cache))[dst] = vv;
+      }
+    }
+  }
   store_rows<D>(a, o, l, rows.row_ok, lo, tok0, h, nl, g);
 }
 
 template <int D, int G>
 hipError_t launch_dg(const PrefillArgs &a, int n_work, hipStream_t st) {
-  if (D == 128 && a.block_size >= 8)
-    hipLaunchKernelGGL((prefill_ring_kernel<G>), dim3(n_work), dim3(kThreads), 0, st, a);
-  else
+  if (D == 128 && a.block_size >= 8) {
+    if (a.k_new)
+      hipLaunchKernelGGL((prefill_ring_kernel<G, true>), dim3(n_work), dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_ring_kernel<G, false>), dim3(n_work), dim3(kThreads), 0, st, a);
+  } else {
     hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(n_work), dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -756,43 +879,49 @@ hipError_t launch_d(int group, const PrefillArgs &a, int n_work, hipStream_t st)
   return hipErrorInvalidValue;
 }
 
-}  // namespace
-
-extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num_q_heads,
-                                  const int32_t *cu_seqlens, int32_t num_seqs, int32_t max_query_len,
-                                  const void *k_cache, const void *v_cache, const pa_cache_t *cache,
-                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                  const int32_t *context_lens, int32_t max_context_len, float scale,
-                                  void *out, int32_t out_dtype, void *stream) {
+// pa_prefill and pa_prefill_write.  Every argument is checked before
+// anything is enqueued.  With k_new set the chunk's rows are stored too: in
+// the attention kernel itself where it loads tiles straight into LDS, else
+// by pa_write_kv ahead of the attention.
+pa_status_t prefill_impl(const char *who, const void *q, int32_t num_tokens, int32_t num_q_heads,
+                         const int32_t *cu_seqlens, int32_t num_seqs, int32_t max_query_len, const void *k_cache,
+                         const void *v_cache, const pa_cache_t *cache, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len,
+                         float scale, void *out, int32_t out_dtype, void *stream, const void *k_new,
+                         const void *v_new, const int64_t *slot_mapping) {
   using pa::fail;
-  if (!cache) return fail(PA_EINVAL, "pa_prefill: cache descriptor is NULL");
+  if (!cache) return fail(PA_EINVAL, "%s: cache descriptor is NULL", who);
   const pa_cache_t c = *cache;
   if (num_tokens < 0 || num_seqs < 0 || max_query_len < 0 || max_context_len < 0 || num_q_heads <= 0 ||
       c.num_blocks <= 0 || c.num_kv_heads <= 0 || c.block_size <= 0 || max_blocks_per_seq <= 0)
-    return fail(PA_EINVAL, "pa_prefill: sizes must be positive (counts may be 0)");
-  if (c.dtype != PA_BF16) return fail(PA_EUNSUPPORTED, "pa_prefill: cache dtype %d (built: bf16)", c.dtype);
+    return fail(PA_EINVAL, "%s: sizes must be positive (counts may be 0)", who);
+  if (c.dtype != PA_BF16) return fail(PA_EUNSUPPORTED, "%s: cache dtype %d (built: bf16)", who, c.dtype);
   if (out_dtype != PA_F32 && out_dtype != PA_BF16)
-    return fail(PA_EUNSUPPORTED, "pa_prefill: out dtype %d (use PA_F32 or PA_BF16)", out_dtype);
+    return fail(PA_EUNSUPPORTED, "%s: out dtype %d (use PA_F32 or PA_BF16)", who, out_dtype);
   if (c.head_dim != 64 && c.head_dim != 128)
-    return fail(PA_EUNSUPPORTED, "pa_prefill: head_dim %d (built: 64, 128)", c.head_dim);
+    return fail(PA_EUNSUPPORTED, "%s: head_dim %d (built: 64, 128)", who, c.head_dim);
   if (c.block_size > 256 || (c.block_size & (c.block_size - 1)))
-    return fail(PA_EUNSUPPORTED, "pa_prefill: block_size %d (powers of two up to 256)", c.block_size);
+    return fail(PA_EUNSUPPORTED, "%s: block_size %d (powers of two up to 256)", who, c.block_size);
   if ((int64_t)c.num_kv_heads * c.block_size > INT32_MAX)
-    return fail(PA_EUNSUPPORTED, "pa_prefill: %d KV heads x block size %d: over 2^31 rows per block", c.num_kv_heads,
-                c.block_size);
+    return fail(PA_EUNSUPPORTED, "%s: %d KV heads x block size %d: over 2^31 rows per block", who,
+                c.num_kv_heads, c.block_size);
   if (num_q_heads % c.num_kv_heads)
-    return fail(PA_EINVAL, "pa_prefill: %d query heads not a multiple of %d KV heads", num_q_heads,
+    return fail(PA_EINVAL, "%s: %d query heads not a multiple of %d KV heads", who, num_q_heads,
                 c.num_kv_heads);
   if (!(scale > 0.0f) || !(scale < INFINITY))
-    return fail(PA_EINVAL, "pa_prefill: scale %g must be positive and finite", (double)scale);
+    return fail(PA_EINVAL, "%s: scale %g must be positive and finite", who, (double)scale);
   const int g = num_q_heads / c.num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
-    return fail(PA_EUNSUPPORTED, "pa_prefill: query heads per KV head = %d (built: 1, 2, 4, 8)", g);
-  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
-  if (!q || !cu_seqlens || !k_cache || !v_cache || !block_tables || !context_lens || !out)
-    return fail(PA_EINVAL, "pa_prefill: NULL pointer");
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) % 16)
-    return fail(PA_EINVAL, "pa_prefill: q, out and the pools must be 16-byte aligned");
+    return fail(PA_EUNSUPPORTED, "%s: query heads per KV head = %d (built: 1, 2, 4, 8)", who, g);
+  const bool store = k_new != nullptr || v_new != nullptr || slot_mapping != nullptr;
+  if (store && num_tokens > 0 && (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache))
+    return fail(PA_EINVAL, "%s: NULL pointer", who);
+  const bool attend = num_seqs > 0 && num_tokens > 0 && max_query_len > 0;
+  if (attend && (!q || !cu_seqlens || !k_cache || !v_cache || !block_tables || !context_lens || !out))
+    return fail(PA_EINVAL, "%s: NULL pointer", who);
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out | (uintptr_t)k_new |
+       (uintptr_t)v_new) % 16)
+    return fail(PA_EINVAL, "%s: q, out, the pools and the stored rows must be 16-byte aligned", who);
 
   int log2_bs = 0;
   while ((1 << log2_bs) < c.block_size) ++log2_bs;
@@ -815,15 +944,53 @@ extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = c.num_blocks;
   a.ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
-  a.q_blocks = (max_query_len + tq - 1) / tq;
+  a.q_blocks = attend ? (max_query_len + tq - 1) / tq : 0;
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   a.qscale = scale * kLog2e;
   const int64_t n_work = (int64_t)num_seqs * a.q_blocks * c.num_kv_heads * (g / gw);
   if (n_work > 0x7fffffff)
-    return fail(PA_EINVAL, "pa_prefill: grid of %lld workgroups too large", (long long)n_work);
+    return fail(PA_EINVAL, "%s: grid of %lld workgroups too large", who, (long long)n_work);
 
+  const bool fused = store && attend && c.head_dim == 128 && c.block_size >= 8;
+  if (store && num_tokens > 0 && !fused)
+    if (pa_status_t st = pa_write_kv(k_new, v_new, slot_mapping, num_tokens, const_cast<void *>(k_cache),
+                                     const_cast<void *>(v_cache), cache, stream))
+      return st;
+  if (!attend) return PA_OK;
+  if (fused) {
+    a.k_new = (const uint4 *)k_new;
+    a.v_new = (const uint4 *)v_new;
+    a.slot_mapping = slot_mapping;
+    a.num_slots = (int64_t)c.num_blocks * c.block_size;
+  }
   const hipStream_t st = (hipStream_t)stream;
   const hipError_t e = c.head_dim == 64 ? launch_d<64>(g, a, (int)n_work, st) : launch_d<128>(g, a, (int)n_work, st);
-  if (e != hipSuccess) return fail(PA_EHIP, "pa_prefill: launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_EHIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" pa_status_t pa_prefill(const void *q, int32_t num_tokens, int32_t num_q_heads,
+                                  const int32_t *cu_seqlens, int32_t num_seqs, int32_t max_query_len,
+                                  const void *k_cache, const void *v_cache, const pa_cache_t *cache,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t max_context_len, float scale,
+                                  void *out, int32_t out_dtype, void *stream) {
+  return prefill_impl("pa_prefill", q, num_tokens, num_q_heads, cu_seqlens, num_seqs, max_query_len, k_cache,
+                      v_cache, cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                      out_dtype, stream, nullptr, nullptr, nullptr);
+}
+
+extern "C" pa_status_t pa_prefill_write(const void *k, const void *v, const int64_t *slot_mapping, const void *q,
+                                        int32_t num_tokens, int32_t num_q_heads, const int32_t *cu_seqlens,
+                                        int32_t num_seqs, int32_t max_query_len, void *k_cache, void *v_cache,
+                                        const pa_cache_t *cache, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                        int32_t max_context_len, float scale, void *out, int32_t out_dtype,
+                                        void *stream) {
+  if (num_tokens > 0 && (!k || !v || !slot_mapping)) return pa::fail(PA_EINVAL, "pa_prefill_write: NULL pointer");
+  return prefill_impl("pa_prefill_write", q, num_tokens, num_q_heads, cu_seqlens, num_seqs, max_query_len, k_cache,
+                      v_cache, cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out,
+                      out_dtype, stream, k, v, slot_mapping);
 }

@@ -77,3 +77,26 @@ def test_prefill_rejects_blocks_over_2_31_rows_before_any_device_call():
                         None, pkv.PA_F32, None)
     assert st == pkv.PA_EUNSUPPORTED
     assert "rows per block" in lib.pa_last_error().decode()
+
+
+def test_prefill_write_argument_errors_before_any_device_call():
+    # every check of pa_prefill_write precedes the first device call, so
+    # these calls run without a GPU
+    lib = pkv.load()
+    cache = pkv.PaCache(num_blocks=8, block_size=16, num_kv_heads=8, head_dim=128, dtype=pkv.PA_BF16)
+    dummy = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its checks first
+
+    def call(k, v, slots, num_tokens=4, q=dummy, head_dim_cache=cache):
+        return lib.pa_prefill_write(k, v, slots, q, num_tokens, 32, dummy, 1, 4, dummy, dummy,
+                                    ctypes.byref(head_dim_cache), dummy, 1, dummy, 16, 0.1, dummy, pkv.PA_F32, None)
+
+    assert call(None, dummy, dummy) == pkv.PA_EINVAL
+    assert "NULL" in lib.pa_last_error().decode()
+    assert call(dummy, dummy, None) == pkv.PA_EINVAL
+    misaligned = ctypes.c_void_p((1 << 20) + 8)
+    assert call(misaligned, dummy, dummy) == pkv.PA_EINVAL
+    assert "16-byte aligned" in lib.pa_last_error().decode()
+    fp32 = pkv.PaCache(num_blocks=8, block_size=16, num_kv_heads=8, head_dim=128, dtype=pkv.PA_F32)
+    assert call(dummy, dummy, dummy, head_dim_cache=fp32) == pkv.PA_EUNSUPPORTED
+    # nothing to store and nothing to attend: a no-op, not an error
+    assert call(None, None, None, num_tokens=0) == pkv.PA_OK
