@@ -224,3 +224,49 @@ def test_needles_strict(gpu_lib, d, bs):
             np.testing.assert_allclose(ref[cu[s] + i], np.broadcast_to(counts / seen, (32, d)), rtol=1e-12, atol=0)
     assert np.isfinite(got).all()
     np.testing.assert_allclose(got, ref, rtol=1e-6, atol=0)
+
+
+def _log2_scores(kind, n):
+    """Scores, in log2 units, that move the softmax's reference max."""
+    t = np.arange(n)
+    if kind == "staircase":  # every 32-key tile passes the previous maximum by about 12
+        return 12.0 * (t // 32)
+    if kind == "crowd":  # one whole tile 6 above the rest: no weight above 2^8, but 8 of them sum past it
+        return np.where(t // 32 == 5, 6.0, 0.0)
+    if kind == "spike":  # one key 20 above the rest
+        return np.where(t == 250, 20.0, 0.0)
+    return -0.05 * t  # falling: the first tile's maximum holds throughout
+
+
+@pytest.mark.parametrize("d,bs", [(128, 16), (64, 16)])
+def test_scores_past_the_running_max(gpu_lib, d, bs):
+    """The kernels keep a reference maximum per row and move it only when a
+    lane's weights against it grow large; scores built to pass it mid-sequence
+    (by ~12 every tile, by 6 across a whole tile, by 20 at one key) and to
+    fall behind it, through channel 0 (q is one-hot there, the other key
+    channels are noise it ignores), must still give the oracle's output."""
+    kinds = ["staircase", "crowd", "spike", "falling"]
+    lens, nq = [800, 600, 500, 300], [800, 600, 200, 300]
+    case = W.make_case(f"running_max_{d}_{bs}", seed=7 + d + bs, dtype=W.BF16, context_lens=lens, num_q_heads=32,
+                       num_kv_heads=8, head_dim=d, block_size=bs, poison=True)
+    rng = np.random.default_rng(d * bs)
+    qscale = float(np.float32(case.scale)) * np.log2(np.e)
+    for s, (kind, ctx) in enumerate(zip(kinds, lens)):
+        k = W.normal(rng, (ctx, 8, d), W.BF16)
+        k[:, :, 0] = W.round_to_bf16((_log2_scores(kind, ctx) / qscale).astype(np.float32))[:, None]
+        v = W.normal(rng, (ctx, 8, d), W.BF16)
+        for t in range(ctx):  # every position, the newest (poisoned) one included
+            blk, off = int(case.block_tables[s, t // bs]), t % bs
+            case.k_cache[blk, :, off, :] = k[t]
+            case.v_cache[blk, :, off, :] = v[t]
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = np.zeros((int(cu[-1]), 32, d), np.uint16)
+    q[:, :, 0] = W.round_to_bf16(np.ones(1, np.float32))[0]
+    ref = P.prefill(q, case.k_cache, case.v_cache, case.block_tables, case.context_lens, cu, case.scale, W.BF16)
+    vmax = float(np.max(np.abs(out_to_f64_np(case.v_cache))))
+    dc = DevCase(case)
+    for od in (torch.float32, None):
+        announce(case.name, "prefill out", od)
+        out = gpu_lib.pa_prefill(to_dev(q), dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, to_dev(cu),
+                                 int(max(nq)), case.max_context, case.scale, out_dtype=od)
+        check_prefill(out_to_f64(out), ref, vmax, bf16_out=od is None)
