@@ -430,6 +430,19 @@ __device__ __forceinline__ int find_seq(const int32_t *cum, int B, int r) {
   return lo;
 }
 
+// The same index found by one whole wave at once: lane l tests whether
+// sequence base + l is the one (cum[s] <= r < cum[s + 1]; exactly one s
+// passes), 64 sequences per step.  Every lane of the wave must be active.
+__device__ __forceinline__ int find_seq_wave(const int32_t *cum, int B, int r) {
+  const int lane = threadIdx.x & 63;
+  for (int base = 0;; base += 64) {
+    const int s = base + lane;
+    const uint64_t hit = __ballot(s < B && cum[s] <= r && r < cum[s + 1]);
+    if (hit) return base + __builtin_ctzll(hit);
+    if (base + 64 >= B) return B - 1;  // not reached while r < cum[B]
+  }
+}
+
 // Balanced split: share w is flattened tokens [w chunk, (w + 1) chunk)
 // of (KV head, sequence, token), every nonempty length rounded up to 16 plus
 // kSegmentCost, with chunk = total / (grid size) rounded up to 16.  The grid is one wave of resident
@@ -465,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   if (a.k_new) {
     constexpr int kChunks = D / 8;  // 16-byte chunks per row
     const int per_tok = a.num_kv_heads * kChunks;
-    for (int tok = blockIdx.x; tok < B; tok += gridDim.x) {
+    for (int tok = blockIdx.x; tok < B; tok += a.num_wg) {
       const int64_t slot = a.slot_mapping[tok];
       for (int ch = tid; ch < per_tok; ch += kThreads) {
         const uint4 kv = a.k_new[(size_t)tok * per_tok + ch];
@@ -482,32 +495,49 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
     }
   }
 
-  // Lengths and the prefix sums of the padded lengths, kThreads sequences at
-  // a time.
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += kThreads) {
-    const int s = base + tid;
-    const int raw = base == 0 ? ctx_first : (s < B ? a.context_lens[s] : 0);
-    const int ctx = raw < 0 ? 0 : (raw > a.ctx_cap ? a.ctx_cap : raw);
-    int v = ctx > 0 ? ((ctx + 15) & ~15) + kSegmentCost<D> : 0;
-    if (s < B) pad[s] = (uint8_t)((v - ctx) | (raw > a.ctx_cap ? kClampedBit : 0));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {  // inclusive scan within the wave
-      const int o = __shfl_up(v, off, 64);
-      if ((tid & 63) >= off) v += o;
+  // Lengths and the prefix sums of the padded lengths.  Up to 64 sequences
+  // wave 0 scans them alone, in registers it keeps for the walk below;
+  // larger batches kThreads sequences at a time.
+  const bool one_wave = B <= 64;
+  int my_len = 0, my_end = 0, my_pad = 0;  // one_wave, lane s of wave 0: sequence s's padded length, cum[s + 1], pad[s]
+  if (one_wave) {
+    if (tid < 64) {
+      const int raw = ctx_first;
+      const int ctx = raw < 0 ? 0 : (raw > a.ctx_cap ? a.ctx_cap : raw);
+      const int v = ctx > 0 ? ((ctx + 15) & ~15) + kSegmentCost<D> : 0;
+      my_pad = (v - ctx) | (raw > a.ctx_cap ? kClampedBit : 0);
+      const int c = wave_incl_scan(v);
+      my_len = v;
+      my_end = c;
+      if (tid < B) {
+        pad[tid] = (uint8_t)my_pad;
+        cum[tid + 1] = c;
+      }
+      if (tid == 0) cum[0] = 0;
     }
-    if ((tid & 63) == 63) wave_tot[tid >> 6] = v;
     __syncthreads();
-    int add = carry;
-    for (int wv = 0; wv < (tid >> 6); ++wv) add += wave_tot[wv];
-    if (s < B) cum[s + 1] = v + add;
+  } else {
+    if (tid == 0) carry = 0;
     __syncthreads();
-    if (tid == kThreads - 1) carry = v + add;
+    for (int base = 0; base < B; base += kThreads) {
+      const int s = base + tid;
+      const int raw = base == 0 ? ctx_first : (s < B ? a.context_lens[s] : 0);
+      const int ctx = raw < 0 ? 0 : (raw > a.ctx_cap ? a.ctx_cap : raw);
+      int v = ctx > 0 ? ((ctx + 15) & ~15) + kSegmentCost<D> : 0;
+      if (s < B) pad[s] = (uint8_t)((v - ctx) | (raw > a.ctx_cap ? kClampedBit : 0));
+      v = wave_incl_scan(v);  // within the wave
+      if ((tid & 63) == 63) wave_tot[tid >> 6] = v;
+      __syncthreads();
+      int add = carry;
+      for (int wv = 0; wv < (tid >> 6); ++wv) add += wave_tot[wv];
+      if (s < B) cum[s + 1] = v + add;
+      __syncthreads();
+      if (tid == kThreads - 1) carry = v + add;
+      __syncthreads();
+    }
+    if (tid == 0) cum[0] = 0;
     __syncthreads();
   }
-  if (tid == 0) cum[0] = 0;
-  __syncthreads();
 
   const int sigma = cum[B];
   const int64_t total = (int64_t)a.num_kv_heads * sigma;
@@ -528,27 +558,50 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   // same time and come from its L2.  Measured on MI355X, 256 sequences
   // sharing a 2048-token prefix: 250 us per copy-on-write step against 398
   // us with share L on workgroup L; unshared batches are unaffected.
-  const int share = xcd_work_id(blockIdx.x, gridDim.x);
+  const int share = xcd_work_id(blockIdx.x, a.num_wg);
   const int64_t f0 = (int64_t)share * chunk;
   const int64_t f1 = min(total, f0 + chunk);
-  const float share_inv = f1 > f0 ? 1.0f / (float)(f1 - f0) : 0.0f;
+  // only steers wave priority: the hardware reciprocal of the share's size (< 2^31) will do
+  const float share_inv = f1 > f0 ? __builtin_amdgcn_rcpf((float)(int)(f1 - f0)) : 0.0f;
   const int log2_bs = a.log2_bs;
 
   // The share [f0, f1) falls into segments, one per (KV head, sequence):
   // tokens [t, e) of the sequence (e clipped to its length), seg flattened
   // positions including the padding.
   const bool small = total <= 0x7fffffff;  // 32-bit division suffices
-  auto segment_at = [&](int64_t f) {
+  // the segment of sequence s at flattened position f, rr = f - kvh sigma
+  auto segment_of = [&](int kvh, int s, int rr, int64_t f) {
     BalSegment g;
-    g.kvh = small ? (int)f / sigma : (int)(f / sigma);
-    const int rr = (int)(f - (int64_t)g.kvh * sigma);
-    g.s = find_seq(cum, B, rr);
-    g.t = rr - cum[g.s];
-    g.lp = cum[g.s + 1] - cum[g.s];
+    g.kvh = kvh;
+    g.s = s;
+    g.t = rr - cum[s];
+    g.lp = cum[s + 1] - cum[s];
     g.seg = (int)min((int64_t)(g.lp - g.t), f1 - f);
-    g.e = max(g.t, min(g.lp - (pad[g.s] & (kClampedBit - 1)), g.t + g.seg));
+    g.e = max(g.t, min(g.lp - (pad[s] & (kClampedBit - 1)), g.t + g.seg));
     g.nblk = g.e > g.t ? ((g.e - 1) >> log2_bs) - (g.t >> log2_bs) + 1 : 0;
     return g;
+  };
+  auto segment_at = [&](int64_t f, bool whole_wave) {
+    const int kvh = small ? (int)f / sigma : (int)(f / sigma);
+    const int rr = (int)(f - (int64_t)kvh * sigma);
+    return segment_of(kvh, whole_wave ? find_seq_wave(cum, B, rr) : find_seq(cum, B, rr), rr, f);
+  };
+  // The segment after g, which ended with its sequence: the next sequence
+  // of the same KV head, or the first of the next one.  Only a run of empty
+  // sequences needs the search (the same segment as segment_at(f) either
+  // way; measured on MI355X, Llama-3-8B-shaped batch: the walk over a share
+  // took 1.76 us of the ~3.6 us before the first tile with a division and a
+  // 6-step search in LDS per segment).
+  auto segment_after = [&](const BalSegment &g, int64_t f) {
+    int kvh = g.kvh, cand = g.s + 1;
+    int rr = (int)(f - (int64_t)kvh * sigma);
+    if (rr >= sigma) {
+      kvh += 1;
+      rr -= sigma;
+      cand = 0;
+    }
+    const int s = cand < B && cum[cand] <= rr && rr < cum[cand + 1] ? cand : find_seq(cum, B, rr);
+    return segment_of(kvh, s, rr, f);
   };
 
   // One walk over the share lists its segments (the first kMaxListedSegs)
@@ -556,22 +609,80 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   // segments than that and their block ids fit in tbl together, they are all
   // staged now in one pass, so that no segment after the first waits for a
   // table load; otherwise each segment is found again and stages its own.
+  // Wave 0 walks alone and leaves the counts in LDS: the walk is scalar
+  // work, and the CU's waves share one scalar unit while every workgroup on
+  // it is in its prologue (measured on MI355X, Llama-3-8B-shaped batch: the
+  // walk took 1.48 us with all four waves walking).
   __shared__ BalSegment segs[kMaxListedSegs];
   __shared__ int seg_off[kMaxListedSegs + 1];  // staged position of each listed segment's first block id
-  int nseg = 0, need = 0;
-  for (int64_t f = f0; f < f1; ++nseg) {
-    const BalSegment g = segment_at(f);
-    if (tid == 0 && nseg < kMaxListedSegs) {
-      segs[nseg] = g;
-      seg_off[nseg] = need;
+  __shared__ int walk_count[2];                // segments, block ids
+  if (tid < 64) {
+    bool walked = false;
+    if (one_wave) {
+      // Every segment at once: lane j takes the j-th (KV head, sequence)
+      // pair from the share's first on, in the flattened order; the
+      // nonempty pairs that start before f1 are the share's segments, in
+      // lane order, the same as the walk below finds one after another.  A
+      // share that reaches past 64 pairs walks instead.
+      const int kvh0 = small ? (int)f0 / sigma : (int)(f0 / sigma);
+      const int rr0 = (int)(f0 - (int64_t)kvh0 * sigma);
+      const int s0 = __builtin_ctzll(__ballot(tid < B && my_end - my_len <= rr0 && rr0 < my_end));
+      const int q = s0 + tid, qk = q / B, sq = q - qk * B;
+      const int kvh = kvh0 + qk;
+      const int lp = __shfl(my_len, sq, 64);
+      const int c0 = __shfl(my_end - my_len, sq, 64);
+      const int pd = __shfl(my_pad, sq, 64);
+      const int t = tid == 0 ? rr0 - c0 : 0;
+      const int64_t fpos = (int64_t)kvh * sigma + c0 + t;
+      const bool valid = lp > 0 && fpos < f1;
+      if (!(__ballot(fpos < f1) >> 63)) {  // lane 63's pair starts at or past f1
+        BalSegment g;
+        g.kvh = kvh;
+        g.s = sq;
+        g.t = t;
+        g.lp = lp;
+        g.seg = (int)min((int64_t)(lp - t), f1 - fpos);
+        g.e = max(t, min(lp - (pd & (kClampedBit - 1)), t + g.seg));
+        g.nblk = valid && g.e > t ? ((g.e - 1) >> log2_bs) - (t >> log2_bs) + 1 : 0;
+        const uint64_t vb = __ballot(valid);
+        const int idx = __popcll(vb & ((1ull << tid) - 1));
+        const int upto = wave_incl_scan(g.nblk);  // block ids of this lane's segment and the ones before it
+        if (valid && idx < kMaxListedSegs) {
+          segs[idx] = g;
+          seg_off[idx] = upto - g.nblk;
+        }
+        const int nseg = __popcll(vb), need = __shfl(upto, 63, 64);
+        if (tid == 0) {
+          walk_count[0] = nseg;
+          walk_count[1] = need;
+          if (nseg <= kMaxListedSegs) seg_off[nseg] = need;
+        }
+        walked = true;
+      }
     }
-    need += g.nblk;
-    f += g.seg;
+    if (!walked) {
+      int nseg = 0, need = 0;
+      BalSegment g;
+      for (int64_t f = f0; f < f1; ++nseg) {
+        g = nseg == 0 ? segment_at(f, true) : segment_after(g, f);
+        if (tid == 0 && nseg < kMaxListedSegs) {
+          segs[nseg] = g;
+          seg_off[nseg] = need;
+        }
+        need += g.nblk;
+        f += g.seg;
+      }
+      if (tid == 0) {
+        walk_count[0] = nseg;
+        walk_count[1] = need;
+        if (nseg <= kMaxListedSegs) seg_off[nseg] = need;
+      }
+    }
   }
+  __syncthreads();
+  const int nseg = walk_count[0], need = walk_count[1];
   const bool listed = nseg <= kMaxListedSegs;
   const bool staged = listed && need <= a.tbl_cap;
-  if (tid == 0 && listed) seg_off[nseg] = need;
-  __syncthreads();
   if (staged) {
     // Every listed segment's block ids in one pass: each thread issues the
     // loads of up to kStageBatch ids (of any segments) before storing any,
@@ -605,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
   int off = 0;
   int64_t f = f0;
   for (int i = 0; f < f1; ++i) {
-    const BalSegment g = listed ? segs[i] : segment_at(f);
+    const BalSegment g = listed ? segs[i] : segment_at(f, false);
     const int s = g.s, kvh = g.kvh, t = g.t, e = g.e, seg = g.seg;
     f += seg;
     const int ctx = g.lp - (pad[s] & (kClampedBit - 1));

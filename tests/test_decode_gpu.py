@@ -219,6 +219,22 @@ def test_balanced_many_sequences_and_empty_ones(gpu_lib):
     run_and_check(gpu_lib, case, [0, BAL])
 
 
+@pytest.mark.parametrize("lens", [
+    [1000] + [0] * 62 + [1000],        # a share runs past 62 empty sequences: the one-at-a-time walk
+    [0, 0, 5, 0, 700, 0, 0, 3, 0, 0],  # empty sequences at both ends and between
+    [4096, 0, 7],                      # shares cross from one KV head to the next
+    [1] * 64,                          # 64 one-token sequences
+])
+def test_balanced_split_of_small_batches(gpu_lib, lens):
+    """Up to 64 sequences one wave scans the lengths and finds every segment
+    of a share at once (a share spanning more than 64 (KV head, sequence)
+    pairs takes them one at a time instead); the split must cover every
+    token of every KV head once, whatever empty sequences lie between."""
+    case = W.make_case(f"small_batch_{len(lens)}_{sum(lens)}", seed=len(lens) + 3, dtype=W.BF16, context_lens=lens,
+                       num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, poison=True)
+    run_and_check(gpu_lib, case, [BAL])
+
+
 def test_balanced_workspace_reuse_garbage_and_repeats(gpu_lib):
     """One balanced-split workspace, filled with random bytes first, serves
     cases of different shapes in turn (one of them a single long sequence cut
