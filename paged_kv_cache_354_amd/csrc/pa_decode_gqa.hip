@@ -626,7 +626,9 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_balanced(DecodeArgs a) {
       // share that reaches past 64 pairs walks instead.
       const int kvh0 = small ? (int)f0 / sigma : (int)(f0 / sigma);
       const int rr0 = (int)(f0 - (int64_t)kvh0 * sigma);
-      const int s0 = __builtin_ctzll(__ballot(tid < B && my_end - my_len <= rr0 && rr0 < my_end));
+      // exactly one sequence holds rr0 (0 <= rr0 < sigma); the guard only keeps ctz defined
+      const uint64_t at0 = __ballot(tid < B && my_end - my_len <= rr0 && rr0 < my_end);
+      const int s0 = at0 ? __builtin_ctzll(at0) : 0;
       const int q = s0 + tid, qk = q / B, sq = q - qk * B;
       const int kvh = kvh0 + qk;
       const int lp = __shfl(my_len, sq, 64);
