@@ -399,12 +399,16 @@ __global__ __launch_bounds__(kThreads) void decode_gqa_kernel(DecodeArgs a) {
 // Every segment a workgroup takes on costs it a fixed time (its first loads
 // and the reduction at its end), so each nonempty sequence's flattened length
 // carries this many extra positions (no tokens) beyond its padding: shares
-// with more segments hold fewer tokens.  The cost is 48 KiB of K/V, at most
-// 96 tokens (96 at head size 128: measured on MI355X on the Llama-3-8B-shaped
-// batch, 0 / 32 / 64 / 96 / 128 / 192 extra tokens gave 109.8 / 109.0 /
-// 108.3 / 107.5 / 108.2 / 108.5 us per call).
+// with more segments hold fewer tokens.  The cost is 24 KiB of K/V (48
+// positions at head size 128, 96 at 64, 32 at 256).  Measured on MI355X,
+// Llama-3-8B-shaped batch, 0 / 16 / 32 / 48 / 64 / 80 / 96 positions:
+// 102.7 / 102.2 / 101.5 / 100.9 / 101.1 / 101.3 / 101.6 us per call; 8 x 32k
+// tokens 174.6 -> 171.7 us at 48 against 96; 256 sequences sharing a prefix
+// unchanged.  (96 was best while each segment waited for its own table
+// round trip and the walk over a share's segments cost more.)
 template <int D>
-constexpr int kSegmentCost = 48 * 1024 / (4 * D) < 96 ? (48 * 1024 / (4 * D) + 15) & ~15 : 96;
+constexpr int kSegmentCost = (24 * 1024 / (4 * D) + 15) & ~15;
+static_assert(kSegmentCost<128> == 48 && kSegmentCost<64> == 96 && kSegmentCost<256> == 32, "segment cost");
 // The LDS byte per sequence holds padding + cost in bits 0..6 and, in bit 7,
 // whether its length was clamped (its newest token is then not attended).
 constexpr int kClampedBit = 0x80;
