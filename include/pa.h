@@ -270,8 +270,9 @@ pa_status_t pa_decode_write_noalloc(const void *k, const void *v, const int64_t 
  *                 queries of all sequences packed in sequence order.
  *   cu_seqlens    device int32 [num_seqs + 1]: sequence s owns query rows
  *                 cu_seqlens[s] .. cu_seqlens[s + 1] - 1 (n_s of them),
- *                 non-decreasing from 0; n_s <= max_query_len (a host bound;
- *                 rows past it are not computed).
+ *                 non-decreasing from 0 to at most num_tokens; n_s <=
+ *                 max_query_len (a host bound; rows past it are not
+ *                 computed).
  *   context_lens  device int32 [num_seqs]: keys of sequence s after its new
  *                 tokens were stored (pa_write_kv); its n_s queries are its
  *                 last n_s positions: query i sits at position

@@ -55,6 +55,7 @@ using pa::exp2_fast;
 using pa::kLog2e;
 using pa::kNegBig;
 using pa::to_bf16;
+using pa::wave_incl_scan;
 using pa::xcd_work_id;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -86,7 +87,8 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t num_blocks;
   int32_t ctx_cap;   // lengths are clamped to this
-  int32_t q_blocks;  // query blocks (of the workgroup's tokens) per sequence in the grid
+  int32_t q_blocks;  // query blocks (of the workgroup's tokens) per sequence, at most
+  int32_t q_items;   // grid slots per (KV head, head group): one per query block
   int32_t out_f32;   // 1: fp32 output, 0: bf16
   float qscale;      // scale * log2(e)
   // Fused store (pa_prefill_write; k_new NULL otherwise): query row r's key
@@ -121,28 +123,36 @@ struct PrefillShared {
 // unequal the sequences are, and an XCD's L2 holds the keys and values of
 // its own heads only.  Longest first within an XCD keeps a long
 // sequence's workgroups from starting last and running alone at the end.
+// In a ranked batch (2 to kRankSeqs sequences) the grid holds only the
+// query blocks that exist: a sequence of n rows has ceil(n / TQ) of them,
+// so the grid is sized from the token count instead of every sequence
+// taking as many as the longest (measured on MI355X, 8 prompts of
+// U{512..4096}: 8,192 workgroups of which 3,392 had no rows, each still
+// dispatched and staging the lengths before it exited).  Wave 0 finds the
+// sequence of query slot `item` from the block counts in rank order.
 struct WorkItem {
   int s, lo, n, ctx;  // sequence, its first query row, its query rows, its context length
   int qb, hg, kvh;    // query block, head group, KV head
 };
 
-template <int HG>
+template <int HG, int TQ>
 __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scratch) {
   WorkItem w;
-  const int n_work = a.num_seqs * a.q_blocks * a.num_kv_heads * HG;
+  const int n_work = a.q_items * a.num_kv_heads * HG;
   int r = xcd_work_id(blockIdx.x, n_work);
-  w.qb = a.q_blocks - 1 - r % a.q_blocks;
-  r /= a.q_blocks;
-  const int rank = r % a.num_seqs;
-  r /= a.num_seqs;
+  const int item = r % a.q_items;
+  r /= a.q_items;
   w.hg = r % HG;
   w.kvh = r / HG;
+  w.qb = a.q_blocks - 1 - item % a.q_blocks;
+  const int rank = item / a.q_blocks;
   if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
     // the sequence of this rank by context length, longest first, ties by
     // index (a permutation, so exactly one sequence has it).  The lengths
     // and the query offsets are staged together, so the choice costs no
     // extra round trip; the scratch is LDS the caller reuses afterwards.
-    __shared__ int chosen;
+    __shared__ int chosen, chosen_qb;
+    __shared__ int by_rank[kRankSeqs], blocks_by_rank[kRankSeqs];
     int32_t *len = scratch;
     int32_t *cu = scratch + kRankSeqs;
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
@@ -160,10 +170,34 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
         const int lj = len[j];
         rk += lj > lt || (lj == lt && j < t);
       }
-      if (rk == rank) chosen = t;
+      by_rank[rk] = t;
+      blocks_by_rank[rk] = min((cu[t + 1] - cu[t] + TQ - 1) / TQ, a.q_blocks);
     }
     __syncthreads();
-    w.s = __builtin_amdgcn_readfirstlane(chosen);
+    if (threadIdx.x < 64) {  // the sequence whose query blocks hold slot `item`, longest first
+      const int lane = threadIdx.x;
+      const int nb = lane < a.num_seqs ? blocks_by_rank[lane] : 0;
+      const int upto = wave_incl_scan(nb);
+      const uint64_t at = __ballot(item >= upto - nb && item < upto);
+      const int rk = at ? __builtin_ctzll(at) : -1;  // none: a slot past the last block
+      if (lane == 0) {
+        chosen = rk >= 0 ? by_rank[rk] : -1;
+        chosen_qb = rk >= 0 ? __builtin_amdgcn_readlane(upto, rk) - 1 - item : 0;
+      }
+    }
+    __syncthreads();
+    const int cs = __builtin_amdgcn_readfirstlane(chosen);
+    if (cs < 0) {
+      w.s = 0;
+      w.lo = 0;
+      w.n = 0;  // nothing to do: the caller returns
+      w.ctx = 0;
+      w.qb = 0;
+      __syncthreads();
+      return w;
+    }
+    w.s = cs;
+    w.qb = __builtin_amdgcn_readfirstlane(chosen_qb);
     w.lo = __builtin_amdgcn_readfirstlane(cu[w.s]);
     w.n = __builtin_amdgcn_readfirstlane(cu[w.s + 1]) - w.lo;
     w.ctx = __builtin_amdgcn_readfirstlane(len[w.s]);
@@ -358,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_kernel(PrefillArgs a) {
   constexpr int OB = D / 16;          // 16-channel blocks of the output
   __shared__ PrefillShared<D> sh;
 
-  const WorkItem wk = find_work<HG>(a, sh.tbl);
+  const WorkItem wk = find_work<HG, TQ>(a, sh.tbl);
   const int s = wk.s, lo = wk.lo, n = wk.n, ctx = wk.ctx, kvh = wk.kvh;
   const int q0 = wk.qb * TQ;
   if (q0 >= n) return;
@@ -613,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   constexpr int OB = D / 16;          // 16-channel blocks of the output
   __shared__ uint4 ring[kRing * kSlot / 16];
 
-  const WorkItem wk = find_work<HG>(a, reinterpret_cast<int32_t *>(ring));
+  const WorkItem wk = find_work<HG, TQ>(a, reinterpret_cast<int32_t *>(ring));
   const int s = wk.s, lo = wk.lo, n = wk.n, ctx = wk.ctx, kvh = wk.kvh;
   const int q0 = wk.qb * TQ;
   if (q0 >= n) return;
@@ -942,9 +976,15 @@ pa_status_t prefill_impl(const char *who, const void *q, int32_t num_tokens, int
   a.num_blocks = c.num_blocks;
   a.ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
   a.q_blocks = attend ? (max_query_len + tq - 1) / tq : 0;
+  // A ranked batch's grid holds the query blocks that exist: sum over s of
+  // ceil(n_s / tq) <= ceil(num_tokens / tq) + num_seqs (the rows are packed).
+  const int64_t all_slots = (int64_t)num_seqs * a.q_blocks;
+  const bool ranked = num_seqs > 1 && num_seqs <= kRankSeqs;
+  const int64_t packed = ((int64_t)num_tokens + tq - 1) / tq + num_seqs;
+  a.q_items = (int32_t)(ranked && packed < all_slots ? packed : all_slots);
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   a.qscale = scale * kLog2e;
-  const int64_t n_work = (int64_t)num_seqs * a.q_blocks * c.num_kv_heads * (g / gw);
+  const int64_t n_work = (int64_t)a.q_items * c.num_kv_heads * (g / gw);
   if (n_work > 0x7fffffff)
     return fail(PA_EINVAL, "%s: grid of %lld workgroups too large", who, (long long)n_work);
 
