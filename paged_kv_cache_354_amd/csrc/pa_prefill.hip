@@ -67,6 +67,7 @@ constexpr int kKeys = 32;      // keys per tile
 constexpr int kRB = 2;         // 16-row blocks per wave
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr int kRankSeqs = 32; // batches up to this many sequences run longest first
+constexpr int kTailSeqs = 8;   // at most this many shortest ones merged by key count
 constexpr float kLazyW = 256.0f;  // headroom of the running max: weights up to 2^8 (8 in log2 units)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
 constexpr int kWaitVmem = 0x0F70;
@@ -89,6 +90,7 @@ struct PrefillArgs {
   int32_t ctx_cap;   // lengths are clamped to this
   int32_t q_blocks;  // query blocks (of the workgroup's tokens) per sequence, at most
   int32_t q_items;   // grid slots per (KV head, head group): one per query block
+  int32_t tail_keys; // ranked batches: context tokens the merged tail may hold per KV head
   int32_t out_f32;   // 1: fp32 output, 0: bf16
   float qscale;      // scale * log2(e)
   // Fused store (pa_prefill_write; k_new NULL otherwise): query row r's key
@@ -130,6 +132,10 @@ struct PrefillShared {
 // U{512..4096}: 8,192 workgroups of which 3,392 had no rows, each still
 // dispatched and staging the lengths before it exited).  Wave 0 finds the
 // sequence of query slot `item` from the block counts in rank order.
+// The shortest contexts, up to kTailSeqs of them whose keys and values fit
+// half an XCD's L2 per KV head, are merged: their query blocks are taken by
+// key count, most first, so the costliest blocks of the last sequences do
+// not start after the cheap ones of the sequences before them.
 struct WorkItem {
   int s, lo, n, ctx;  // sequence, its first query row, its query rows, its context length
   int qb, hg, kvh;    // query block, head group, KV head
@@ -153,6 +159,7 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
     // extra round trip; the scratch is LDS the caller reuses afterwards.
     __shared__ int chosen, chosen_qb;
     __shared__ int by_rank[kRankSeqs], blocks_by_rank[kRankSeqs];
+    __shared__ int first_by_rank[kRankSeqs], rows_by_rank[kRankSeqs];
     int32_t *len = scratch;
     int32_t *cu = scratch + kRankSeqs;
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
@@ -170,19 +177,69 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
         const int lj = len[j];
         rk += lj > lt || (lj == lt && j < t);
       }
+      const int rows = cu[t + 1] - cu[t];
       by_rank[rk] = t;
-      blocks_by_rank[rk] = min((cu[t + 1] - cu[t] + TQ - 1) / TQ, a.q_blocks);
+      blocks_by_rank[rk] = min((rows + TQ - 1) / TQ, a.q_blocks);
+      first_by_rank[rk] = lt - rows;
+      rows_by_rank[rk] = rows;
     }
     __syncthreads();
-    if (threadIdx.x < 64) {  // the sequence whose query blocks hold slot `item`, longest first
+    if (threadIdx.x < 64) {  // the sequence and query block of slot `item`
       const int lane = threadIdx.x;
-      const int nb = lane < a.num_seqs ? blocks_by_rank[lane] : 0;
+      const int B = a.num_seqs;
+      const int nb = lane < B ? blocks_by_rank[lane] : 0;
       const int upto = wave_incl_scan(nb);
-      const uint64_t at = __ballot(item >= upto - nb && item < upto);
-      const int rk = at ? __builtin_ctzll(at) : -1;  // none: a slot past the last block
+      const int total = __builtin_amdgcn_readlane(upto, B - 1);
+      // The tail: the last ranks, at most kTailSeqs, whose contexts sum to
+      // at most tail_keys (lane l adds the context of rank B - 1 - l).
+      const int back = lane < B ? len[by_rank[B - 1 - lane]] : 0;
+      const int upto_back = wave_incl_scan(back);
+      int k = __popcll(__ballot(lane < B && lane < kTailSeqs && upto_back <= a.tail_keys));
+      if (k < 2) k = 0;
+      const int t0 = k == 0 ? total : (k == B ? 0 : __builtin_amdgcn_readlane(upto, B - 1 - k));
       if (lane == 0) {
-        chosen = rk >= 0 ? by_rank[rk] : -1;
-        chosen_qb = rk >= 0 ? __builtin_amdgcn_readlane(upto, rk) - 1 - item : 0;
+        chosen = -1;  // a slot past the last block
+        chosen_qb = 0;
+      }
+      if (item < t0) {  // rank by rank, each one's blocks last first
+        const uint64_t at = __ballot(item >= upto - nb && item < upto);
+        const int rk = at ? __builtin_ctzll(at) : -1;
+        if (lane == 0 && rk >= 0) {
+          chosen = by_rank[rk];
+          chosen_qb = __builtin_amdgcn_readlane(upto, rk) - 1 - item;
+        }
+      } else if (item < total) {
+        // The tail's blocks merged by key count, most first (ties by rank):
+        // a block's place is the number of blocks before it, counted per
+        // rank in closed form since a rank's keys grow with its block.
+        // Exactly one (rank, block) has place `item - t0`.
+        const int j = item - t0;
+        const int f = lane < B ? first_by_rank[lane] : 0;
+        const int nr = lane < B ? rows_by_rank[lane] : 0;
+        for (int r1 = B - k; r1 < B; ++r1) {
+          const int nb1 = __builtin_amdgcn_readlane(nb, r1);
+          const int f1 = __builtin_amdgcn_readlane(f, r1);
+          const int n1 = __builtin_amdgcn_readlane(nr, r1);
+          for (int qb = lane; qb < nb1; qb += 64) {
+            const int key = f1 + min((qb + 1) * TQ, n1);
+            int place = nb1 - 1 - qb;
+            for (int r2 = B - k; r2 < B; ++r2) {
+              if (r2 == r1) continue;
+              const int nb2 = __builtin_amdgcn_readlane(nb, r2);
+              const int f2 = __builtin_amdgcn_readlane(f, r2);
+              const int n2 = __builtin_amdgcn_readlane(nr, r2);
+              // blocks of r2 with key above `key`, or equal to it when r2 < r1
+              const int below = key - (r2 > r1 ? 0 : 1);  // their keys <= below come after
+              const int d = below - f2;
+              const int after = below >= f2 + n2 ? nb2 : (d < TQ ? 0 : min(d / TQ, nb2));
+              place += nb2 - after;
+            }
+            if (place == j) {
+              chosen = by_rank[r1];
+              chosen_qb = qb;
+            }
+          }
+        }
       }
     }
     __syncthreads();
@@ -982,6 +1039,9 @@ pa_status_t prefill_impl(const char *who, const void *q, int32_t num_tokens, int
   const bool ranked = num_seqs > 1 && num_seqs <= kRankSeqs;
   const int64_t packed = ((int64_t)num_tokens + tq - 1) / tq + num_seqs;
   a.q_items = (int32_t)(ranked && packed < all_slots ? packed : all_slots);
+  // The merged tail's keys and values (2 bytes each of K and V per channel
+  // and token) stay within 2 MiB per KV head, half an XCD's L2.
+  a.tail_keys = (2 << 20) / (4 * c.head_dim);
   a.out_f32 = out_dtype == PA_F32 ? 1 : 0;
   a.qscale = scale * kLog2e;
   const int64_t n_work = (int64_t)a.q_items * c.num_kv_heads * (g / gw);

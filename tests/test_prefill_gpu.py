@@ -97,6 +97,26 @@ def test_length_ordered_work_with_ties(gpu_lib, nseq):
     run_case(gpu_lib, case, q, cu)
 
 
+# In a batch of 2..32 sequences the shortest contexts, up to 8 of them
+# holding at most 2 MiB of keys and values per KV head (4,096 tokens at
+# head_dim 128, 8,192 at 64), run their query blocks merged by key count.
+# Cases: a tail of 8 equal lengths summing to exactly the bound (equal keys,
+# ties by index) and one token over it (7 merged), chunks whose blocks end on the same key in different
+# sequences, empty chunks and chunks past the context inside the tail,
+# 64- and 128-row query blocks (2 and 1 query heads per KV head), head_dim 64.
+@pytest.mark.parametrize("lens,nq,hq,hkv,d", [
+    ([600] + [512] * 8, [600] + [512] * 8, 32, 8, 128),
+    ([600, 513] + [512] * 7, [600, 513] + [512] * 7, 32, 8, 128),
+    ([600, 600, 332, 300, 700, 96, 64], [64, 32, 64, 0, 100, 96, 80], 32, 8, 128),
+    ([900, 500, 500, 260, 130, 129], [900, 500, 244, 260, 130, 1], 8, 8, 128),
+    ([700, 450, 450, 200, 77], [300, 450, 450, 200, 77], 16, 8, 128),
+    ([5000, 4100, 4092, 3000, 100], [64, 256, 300, 1000, 100], 32, 8, 64),
+])
+def test_merged_tail_of_short_sequences(gpu_lib, lens, nq, hq, hkv, d):
+    case, q, cu = make_prefill(sum(lens) + hq + d, lens, nq, hq, hkv, d, 16)
+    run_case(gpu_lib, case, q, cu)
+
+
 def test_chunk_longer_than_context_gives_zero_rows(gpu_lib):
     case, q, cu = make_prefill(31, [5, 40], [9, 40], 32, 8, 128, 16)
     dc = run_case(gpu_lib, case, q, cu)
