@@ -335,8 +335,12 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
       // and the compiler would otherwise turn the mask into selects that
       // every tile pays for (an empty volatile asm cannot be speculated).
       asm volatile("");
-      // key kt0 + 16hh + 4g + e lies past the row when 16hh + e > lim
-      const int lim = prow[rb] - kt0 - 4 * g;
+      // key kt0 + 16hh + 4g + e lies past the row when 16hh + e > lim.
+      // kt0 passes through an empty asm so that lim is formed here, not
+      // stepped on every tile as an induction variable.
+      int kt = kt0;
+      asm("" : "+s"(kt));
+      const int lim = prow[rb] - 4 * g - kt;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -809,6 +813,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   const uint64_t knew = (uint64_t)(uintptr_t)a.k_new + (uint64_t)kvh * kRowBytes;
   const uint64_t vnew = (uint64_t)(uintptr_t)a.v_new + (uint64_t)kvh * kRowBytes;
   auto new_row_at = [&](int p) -> uint64_t { return (uint64_t)(uint32_t)(lo + p - first_pos) * new_row_bytes; };
+  const uint32_t lane_new_off = ((lane >> 2) & 3) * new_row_bytes + lane_seg;
 
   // The table entry of group grp (keys 32u + 8 wave + 4 grp ..) of tile u.
   // A group's 4 keys share a block (block size >= 8, groups 4-aligned).
@@ -830,13 +835,20 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       if (WRITE && min(kt + 3, kend - 1) >= first_pos) {  // uniform: the group holds keys of the chunk
         const uint32_t kdst = __builtin_amdgcn_readfirstlane(slot + qg * kGrp);
         const uint32_t vdst = __builtin_amdgcn_readfirstlane(slot + kSlotK + qg * kGrp);
-        const int p = min(kt + ((lane >> 2) & 3), kend - 1);  // the lane's key
         if (kt >= first_pos) {  // all from the chunk's rows
           const int key0 = min(kt, kend - 1);
-          const uint32_t voff = (uint32_t)(p - key0) * new_row_bytes + lane_seg;
+          // the lane's row offset is a lane constant unless the group
+          // reaches kend (uniform; a real branch, as for the causal mask)
+          uint32_t voff = lane_new_off;
+          if (kt + 3 >= kend) {
+            asm volatile("");
+            const int p = min(kt + ((lane >> 2) & 3), kend - 1);  // the lane's key
+            voff = (uint32_t)(p - key0) * new_row_bytes + lane_seg;
+          }
           load_lds16(uniform64(knew + new_row_at(key0)), voff, kdst);
           load_lds16(uniform64(vnew + new_row_at(key0)), voff, vdst);
         } else {  // keys before first_pos from the pool (block of kt), the rest from the chunk's rows
+          const int p = min(kt + ((lane >> 2) & 3), kend - 1);  // the lane's key
           const int blk = grp ? blk1 : blk0;
           const uint32_t pb = (unsigned)blk < (unsigned)a.num_blocks ? (uint32_t)blk : 0u;
           const uint64_t pool = (uint64_t)pb * block_bytes + (uint64_t)(p & bmask) * kRowBytes + lane_seg;
@@ -849,7 +861,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       }
       int key0 = kt;
       uint32_t voff = lane_off;
-      if (kt + 3 >= kend) {  // uniform: the group reaches kend
+      if (kt + 3 >= kend) {  // uniform: the group reaches kend (a real branch)
+        asm volatile("");
         key0 = min(kt, kend - 1);
         voff = (uint32_t)(min(kt + ((lane >> 2) & 3), kend - 1) - key0) * kRowBytes + (lane >> 4) * 64 + (lane & 3) * 16;
       }
@@ -869,8 +882,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   const uint32_t k_lane = (nl >> 2) * kGrp + (nl & 3) * 64 + g * 16;
   const uint32_t v_lane = g * kGrp + (nl >> 2) * 64 + ((nl >> 1) & 1) * 16 + (nl & 1) * 8;
 
+  const uint32_t k_at = ring0 + k_lane, v_at = ring0 + kSlotK + v_lane;
+
   const int ntiles = (kend + kKeys - 1) / kKeys;
   int nb0 = 0, nb1 = 0;  // block ids of the tile loaded next
+  // (t % kRing) * kSlot, stepped in a scalar register: one vector add per
+  // read address and tile (the compiler had rebuilt it from t * kSlot and
+  // t / 3 with two)
+  uint32_t slot_off = 0;
   if (ntiles > 0) load_tile(0, block_of(0, 0), block_of(0, 1));
   if (ntiles > 1) load_tile(1, block_of(1, 0), block_of(1, 1));
   if (ntiles > 2) {
@@ -892,8 +911,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       // keeps the compiler from folding the slot into per-read constants and
       // hoisting those out of the loop (16 registers, and two adds per read),
       // so every read below is the register plus an immediate offset.
-      const uint32_t slot = ring0 + (uint32_t)(t % kRing) * kSlot;
-      uint32_t ka = slot + k_lane, va = slot + kSlotK + v_lane;
+      uint32_t ka = k_at + slot_off, va = v_at + slot_off;
       asm("" : "+v"(ka), "+v"(va));
       // half the V^T operands read before the softmax (measured on MI355X:
       // 1-1.5% faster on whole prompts, 0.6% on chunks; all of them do not
@@ -915,6 +933,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       nb0 = block_of(t + 3, 0);
       nb1 = block_of(t + 3, 1);
     }
+    slot_off = slot_off == (kRing - 1) * kSlot ? 0u : slot_off + kSlot;
+    asm("" : "+s"(slot_off));
   }
   if constexpr (WRITE && kStoreFromLds) {
     // Row i of the workgroup's tokens (position first_pos + q0 + i) is key
