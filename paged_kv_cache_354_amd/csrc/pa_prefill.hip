@@ -135,7 +135,9 @@ struct PrefillShared {
 // The shortest contexts, up to kTailSeqs of them whose keys and values fit
 // half an XCD's L2 per KV head, are merged: their query blocks are taken by
 // key count, most first, so the costliest blocks of the last sequences do
-// not start after the cheap ones of the sequences before them.
+// not start after the cheap ones of the sequences before them (measured on
+// MI355X, 8 prompts of U{512..4096}: 1.8% faster per call; merging all of
+// them, 9% slower: one XCD's L2 no longer holds the keys in use).
 struct WorkItem {
   int s, lo, n, ctx;  // sequence, its first query row, its query rows, its context length
   int qb, hg, kvh;    // query block, head group, KV head
