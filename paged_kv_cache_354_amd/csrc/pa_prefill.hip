@@ -67,6 +67,7 @@ constexpr int kKeys = 32;      // keys per tile
 constexpr int kRB = 2;         // 16-row blocks per wave
 constexpr int kTblLds = 2048;  // block ids of a workgroup's keys staged in LDS (else read from HBM)
 constexpr int kRankSeqs = 32; // batches up to this many sequences run longest first
+constexpr int kCompactSeqs = 64;  // and up to this many get a grid of only the query blocks that exist
 constexpr int kTailSeqs = 8;   // at most this many shortest ones merged by key count
 constexpr float kLazyW = 256.0f;  // headroom of the running max: weights up to 2^8 (8 in log2 units)
 // s_waitcnt operand: vmcnt(0) (expcnt and lgkmcnt at their maxima: no wait)
@@ -125,13 +126,14 @@ struct PrefillShared {
 // unequal the sequences are, and an XCD's L2 holds the keys and values of
 // its own heads only.  Longest first within an XCD keeps a long
 // sequence's workgroups from starting last and running alone at the end.
-// In a ranked batch (2 to kRankSeqs sequences) the grid holds only the
-// query blocks that exist: a sequence of n rows has ceil(n / TQ) of them,
-// so the grid is sized from the token count instead of every sequence
-// taking as many as the longest (measured on MI355X, 8 prompts of
-// U{512..4096}: 8,192 workgroups of which 3,392 had no rows, each still
-// dispatched and staging the lengths before it exited).  Wave 0 finds the
-// sequence of query slot `item` from the block counts in rank order.
+// In a batch of 2 to kCompactSeqs sequences the grid holds only the query
+// blocks that exist: a sequence of n rows has ceil(n / TQ) of them, so the
+// grid is sized from the token count instead of every sequence taking as
+// many as the longest (measured on MI355X, 8 prompts of U{512..4096}: 8,192
+// workgroups of which 3,392 had no rows, each still dispatched and staging
+// the lengths before it exited).  Wave 0 finds the sequence of query slot
+// `item` from the block counts in rank order (index order past kRankSeqs
+// sequences: ranking 64 prefix-cached suffixes cost more than it gained).
 // The shortest contexts, up to kTailSeqs of them whose keys and values fit
 // half an XCD's L2 per KV head, are merged: their query blocks are taken by
 // key count, most first, so the costliest blocks of the last sequences do
@@ -154,16 +156,17 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
   w.kvh = r / HG;
   w.qb = a.q_blocks - 1 - item % a.q_blocks;
   const int rank = item / a.q_blocks;
-  if (a.num_seqs > 1 && a.num_seqs <= kRankSeqs) {
-    // the sequence of this rank by context length, longest first, ties by
-    // index (a permutation, so exactly one sequence has it).  The lengths
-    // and the query offsets are staged together, so the choice costs no
-    // extra round trip; the scratch is LDS the caller reuses afterwards.
+  if (a.num_seqs > 1 && a.num_seqs <= kCompactSeqs) {
+    // Ranks: by context length, longest first, ties by index (a
+    // permutation, so exactly one sequence has each), or the index itself
+    // past kRankSeqs sequences.  The lengths and the query offsets are
+    // staged together, so this costs no extra round trip; the scratch is
+    // LDS the caller reuses afterwards.
     __shared__ int chosen, chosen_qb;
-    __shared__ int by_rank[kRankSeqs], blocks_by_rank[kRankSeqs];
-    __shared__ int first_by_rank[kRankSeqs], rows_by_rank[kRankSeqs];
+    __shared__ int by_rank[kCompactSeqs], blocks_by_rank[kCompactSeqs];
+    __shared__ int first_by_rank[kCompactSeqs], rows_by_rank[kCompactSeqs];
     int32_t *len = scratch;
-    int32_t *cu = scratch + kRankSeqs;
+    int32_t *cu = scratch + kCompactSeqs;
     for (int i = threadIdx.x; i <= a.num_seqs; i += kThreads) {
       cu[i] = a.cu_seqlens[i];
       if (i < a.num_seqs) {
@@ -172,13 +175,15 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
       }
     }
     __syncthreads();
+    const bool ranked = a.num_seqs <= kRankSeqs;
     for (int t = threadIdx.x; t < a.num_seqs; t += kThreads) {
       const int lt = len[t];
-      int rk = 0;
-      for (int j = 0; j < a.num_seqs; ++j) {
-        const int lj = len[j];
-        rk += lj > lt || (lj == lt && j < t);
-      }
+      int rk = ranked ? 0 : t;
+      if (ranked)
+        for (int j = 0; j < a.num_seqs; ++j) {
+          const int lj = len[j];
+          rk += lj > lt || (lj == lt && j < t);
+        }
       const int rows = cu[t + 1] - cu[t];
       by_rank[rk] = t;
       blocks_by_rank[rk] = min((rows + TQ - 1) / TQ, a.q_blocks);
@@ -197,7 +202,7 @@ __device__ __forceinline__ WorkItem find_work(const PrefillArgs &a, int32_t *scr
       const int back = lane < B ? len[by_rank[B - 1 - lane]] : 0;
       const int upto_back = wave_incl_scan(back);
       int k = __popcll(__ballot(lane < B && lane < kTailSeqs && upto_back <= a.tail_keys));
-      if (k < 2) k = 0;
+      if (k < 2 || !ranked) k = 0;
       const int t0 = k == 0 ? total : (k == B ? 0 : __builtin_amdgcn_readlane(upto, B - 1 - k));
       if (lane == 0) {
         chosen = -1;  // a slot past the last block
@@ -1055,12 +1060,13 @@ pa_status_t prefill_impl(const char *who, const void *q, int32_t num_tokens, int
   a.num_blocks = c.num_blocks;
   a.ctx_cap = (int32_t)(cap64 < max_context_len ? cap64 : max_context_len);
   a.q_blocks = attend ? (max_query_len + tq - 1) / tq : 0;
-  // A ranked batch's grid holds the query blocks that exist: sum over s of
-  // ceil(n_s / tq) <= ceil(num_tokens / tq) + num_seqs (the rows are packed).
+  // A batch of 2 to kCompactSeqs sequences gets a grid of the query blocks
+  // that exist: sum over s of ceil(n_s / tq) <= ceil(num_tokens / tq) +
+  // num_seqs (the rows are packed).
   const int64_t all_slots = (int64_t)num_seqs * a.q_blocks;
-  const bool ranked = num_seqs > 1 && num_seqs <= kRankSeqs;
+  const bool compact = num_seqs > 1 && num_seqs <= kCompactSeqs;
   const int64_t packed = ((int64_t)num_tokens + tq - 1) / tq + num_seqs;
-  a.q_items = (int32_t)(ranked && packed < all_slots ? packed : all_slots);
+  a.q_items = (int32_t)(compact && packed < all_slots ? packed : all_slots);
   // The merged tail's keys and values (2 bytes each of K and V per channel
   // and token) stay within 2 MiB per KV head, half an XCD's L2.
   a.tail_keys = (2 << 20) / (4 * c.head_dim);

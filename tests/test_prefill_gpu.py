@@ -86,10 +86,11 @@ def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
     run_case(gpu_lib, case, q, cu)
 
 
-@pytest.mark.parametrize("nseq", [1, 32, 33])
+@pytest.mark.parametrize("nseq", [1, 32, 33, 64, 65])
 def test_length_ordered_work_with_ties(gpu_lib, nseq):
     # batches of 2..32 sequences are taken longest context first (ties by
-    # index), larger ones in index order; repeated lengths make ties
+    # index), larger ones in index order; repeated lengths make ties.  Up to
+    # 64 sequences the grid holds only the query blocks that exist.
     rng = np.random.default_rng(71 + nseq)
     lens = [int(x) for x in rng.choice([16, 48, 48, 130, 1], size=nseq)]
     nq = [int(min(l, x)) for l, x in zip(lens, rng.integers(0, 40, size=nseq))]
