@@ -118,6 +118,27 @@ def test_merged_tail_of_short_sequences(gpu_lib, lens, nq, hq, hkv, d):
     run_case(gpu_lib, case, q, cu)
 
 
+@pytest.mark.parametrize("seed", range(300, 312))
+def test_random_batches(gpu_lib, seed):
+    # seeded random batches over the work lookup's branches: 1 to 64
+    # sequences (ranked up to 32, compact grid up to 64), whole prompts,
+    # chunks after cached keys, empty chunks and chunks past their context;
+    # both kernels (head_dim 128 at block size 8+ loads tiles into LDS)
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.choice([1, 2, 5, 17, 32, 33, 48, 64]))
+    hkv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([1, 8, 16, 32, 256]))
+    lens = [int(x) for x in rng.integers(1, 600, size=nseq)]
+    nq = []
+    for l in lens:
+        kind = rng.integers(4)
+        nq.append(l if kind == 0 else int(rng.integers(0, min(l, 200) + 1)) if kind < 3 else min(l + 7, 200))
+    case, q, cu = make_prefill(seed, lens, nq, hkv * g, hkv, d, bs)
+    run_case(gpu_lib, case, q, cu)
+
+
 def test_chunk_longer_than_context_gives_zero_rows(gpu_lib):
     case, q, cu = make_prefill(31, [5, 40], [9, 40], 32, 8, 128, 16)
     dc = run_case(gpu_lib, case, q, cu)
