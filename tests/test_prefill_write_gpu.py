@@ -72,6 +72,27 @@ def test_chunks_after_cached_contexts(gpu_lib, hq, hkv, d, bs):
     check_fused_equals_two_calls(gpu_lib, pc)
 
 
+@pytest.mark.parametrize("seed", range(400, 410))
+def test_random_batches(gpu_lib, seed):
+    # seeded random batches: 2 to 64 sequences, whole prompts (chunk =
+    # context), chunks after cached keys (the fused kernel's input-row,
+    # mixed and pool loads), empty chunks and chunks past their context
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.choice([2, 5, 17, 33, 64]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    bs = int(rng.choice([4, 8, 16, 32, 256]))
+    lens = [int(x) for x in rng.integers(1, 900, size=nseq)]
+    chunks = []
+    for l in lens:
+        kind = rng.integers(4)
+        chunks.append(l if kind == 0 else int(rng.integers(0, min(l, 300) + 1)) if kind < 3 else l + int(rng.integers(1, 9)))
+    pc = W.make_prefill(f"prefill_write_random_{seed}", seed=seed, context_lens=lens, chunk_lens=chunks,
+                        num_q_heads=8 * g, num_kv_heads=8, head_dim=d, block_size=bs, poison=True)
+    poison_chunk_slots(pc)
+    check_fused_equals_two_calls(gpu_lib, pc)
+
+
 def test_whole_prompts_many_tiles(gpu_lib):
     pc = W.make_prefill("prefill_write_prompts", seed=41, context_lens=[1500, 37, 900, 4], num_q_heads=32,
                         num_kv_heads=8, head_dim=128, block_size=16, poison=True)
