@@ -86,7 +86,7 @@ def test_prompts_and_chunks(gpu_lib, hq, hkv, d, bs):
     run_case(gpu_lib, case, q, cu)
 
 
-@pytest.mark.parametrize("nseq", [1, 32, 33, 64, 65])
+@pytest.mark.parametrize("nseq", [1, 32, 33, 64, 65, 100])
 def test_length_ordered_work_with_ties(gpu_lib, nseq):
     # batches of 2..32 sequences are taken longest context first (ties by
     # index), larger ones in index order; repeated lengths make ties.  Up to
