@@ -833,8 +833,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   // This wave's loads of tile u (4 instructions): its two groups of K and V.
   // Keys at or past kend read key kend - 1 instead (a real key, finite; the
   // causal mask gives every such key weight 0).
-  auto load_tile = [&](int u, int blk0, int blk1) {
-    const uint32_t slot = ring0 + (uint32_t)(u % kRing) * kSlot;
+  auto load_tile = [&](int u, int slot_idx, int blk0, int blk1) {  // slot_idx = u % kRing
+    const uint32_t slot = ring0 + (uint32_t)slot_idx * kSlot;
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp) {
       const int qg = 2 * wave + grp;
@@ -896,14 +896,16 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
   // (t % kRing) * kSlot, stepped in a scalar register: one vector add per
   // read address and tile (the compiler had rebuilt it from t * kSlot and
   // t / 3 with two)
-  uint32_t slot_off = 0;
-  if (ntiles > 0) load_tile(0, block_of(0, 0), block_of(0, 1));
-  if (ntiles > 1) load_tile(1, block_of(1, 0), block_of(1, 1));
+  if (ntiles > 0) load_tile(0, 0, block_of(0, 0), block_of(0, 1));
+  if (ntiles > 1) load_tile(1, 1, block_of(1, 0), block_of(1, 1));
   if (ntiles > 2) {
     nb0 = block_of(2, 0);
     nb1 = block_of(2, 1);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  // The tile loop, unrolled by the ring's three slots so that each copy's
+  // slot is a constant.
+  auto tile_step = [&](int t, auto slot_tag) {
+    constexpr uint32_t SLOT = decltype(slot_tag)::value;
     // this wave's loads of tile t have landed (those of t + 1 may not), then
     // every wave's have
     if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(kWaitVmem4);
@@ -911,15 +913,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
     __syncthreads();
     // tile t + 2 goes to the slot of tile t - 1, which every wave finished
     // reading before the barrier
-    if (t + 2 < ntiles) load_tile(t + 2, nb0, nb1);
+    if (t + 2 < ntiles) load_tile(t + 2, (SLOT + 2) % kRing, nb0, nb1);
     const int kt0 = t * kKeys;
     if (kt0 < wkend) {
-      // The tile's K and V^T read addresses, one register each; the empty asm
-      // keeps the compiler from folding the slot into per-read constants and
-      // hoisting those out of the loop (16 registers, and two adds per read),
-      // so every read below is the register plus an immediate offset.
-      uint32_t ka = k_at + slot_off, va = v_at + slot_off;
-      asm("" : "+v"(ka), "+v"(va));
+      // The tile's K and V^T reads: a loop-invariant lane base plus an
+      // immediate offset (the slot is a constant of this copy of the body,
+      // and every offset stays below 64 KiB), no per-tile address work.
+      const uint32_t ka = k_at + SLOT * kSlot, va = v_at + SLOT * kSlot;
       // half the V^T operands read before the softmax (measured on MI355X:
       // 1-1.5% faster on whole prompts, 0.6% on chunks; all of them do not
       // fit three workgroups per CU)
@@ -940,8 +940,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_ring_kernel(PrefillArgs a
       nb0 = block_of(t + 3, 0);
       nb1 = block_of(t + 3, 1);
     }
-    slot_off = slot_off == (kRing - 1) * kSlot ? 0u : slot_off + kSlot;
-    asm("" : "+s"(slot_off));
+  };
+  for (int t = 0; t < ntiles; t += kRing) {
+    tile_step(t, std::integral_constant<uint32_t, 0>{});
+    if (t + 1 >= ntiles) break;
+    tile_step(t + 1, std::integral_constant<uint32_t, 1>{});
+    if (t + 2 >= ntiles) break;
+    tile_step(t + 2, std::integral_constant<uint32_t, 2>{});
   }
   if constexpr (WRITE && kStoreFromLds) {
     // Row i of the workgroup's tokens (position first_pos + q0 + i) is key
