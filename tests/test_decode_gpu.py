@@ -239,8 +239,9 @@ def test_balanced_split_of_small_batches(gpu_lib, lens):
 def test_balanced_random_shapes(gpu_lib, seed):
     """Seeded random batches for the balanced split: 1 to 300 sequences (both
     sides of the one-wave scan's 64), lengths from 0 to 3,000 with runs of
-    empty sequences, 4 or 8 query heads per KV head, head_dim 64 or 128,
-    blocks of 8, 16 or 32 tokens."""
+    empty sequences, 4 or 8 query heads per KV head (1 or 2: the vector-ALU
+    kernel's 1024-token partitions under the same mode), head_dim 64 or
+    128, blocks of 8, 16 or 32 tokens."""
     rng = np.random.default_rng(seed)
     b = int(rng.choice([1, 2, 3, 7, 33, 63, 64, 65, 130, 300]))
     lens = rng.integers(0, 3001, size=b) if b <= 64 else rng.integers(0, 400, size=b)
@@ -249,7 +250,7 @@ def test_balanced_random_shapes(gpu_lib, seed):
         start = int(rng.integers(0, b - 3))
         lens[start:start + int(rng.integers(2, min(b - start, 40) + 1))] = 0
     hkv = int(rng.choice([2, 4, 8]))
-    g = int(rng.choice([4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
     d = int(rng.choice([64, 128]))
     bs = int(rng.choice([8, 16, 32]))
     case = W.make_case(f"balanced_random_{seed}", seed=seed, dtype=W.BF16, context_lens=lens, num_q_heads=g * hkv,
