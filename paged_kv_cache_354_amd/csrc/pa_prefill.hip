@@ -292,9 +292,11 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
   constexpr int OB = D / 16;
   __builtin_amdgcn_s_setprio(0);
   // The scheduler's interleaving of matrix ops with LDS reads (strategy 1)
-  // for this region and the P V^T one below (measured on MI355X, four
-  // alternating passes: whole prompts 416.2 -> 408.7 us per fused call,
-  // chunks 605.4 -> 595.8 us; strategy 0 about half that).
+  // for this region (measured on MI355X, alternating passes: with it here
+  // and in the P V^T region, whole prompts 416.2 -> 408.7 us per fused
+  // call, chunks 605.4 -> 595.8 us; here only, a further 0.4-0.5%; in the
+  // P V^T region only, slower; strategy 0 about half the gain, 2 and 3
+  // slower).
   __builtin_amdgcn_iglp_opt(1);
   // S^T for the two 16-key halves of both row blocks; each K operand
   // read from LDS feeds both blocks.  A half's K operands are read just
@@ -394,7 +396,6 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
     pb[rb] = __builtin_convertvector(p, bf16x8_t);
   }
   __builtin_amdgcn_s_setprio(0);
-  __builtin_amdgcn_iglp_opt(1);
   // O^T += V^T P^T, keys in the lane's order (4g..4g+3, 16+4g..16+4g+3).
 #pragma unroll
   for (int j = 0; j < OB; ++j) {
