@@ -344,7 +344,7 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int e = 0; e < 4; ++e) z[4 * hh + e] = st[rb][hh][e];
-    if (diag) {
+    if (__builtin_expect(diag, 0)) {  // rare: laid out off the common path
       // A real branch: most tiles lie wholly below the block's first row,
       // and the compiler would otherwise turn the mask into selects that
       // every tile pays for (an empty volatile asm cannot be speculated).
@@ -375,7 +375,8 @@ __device__ __forceinline__ void attend_tile(KOp kop_at, VOp vop_at, const uint4 
 #pragma unroll
     for (int e = 0; e < 8; ++e) p[e] = exp2_fast(fmaf(z[e], qscale, -m[rb]));
     float ps = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    if (__any(ps > kLazyW)) {
+    if (__builtin_expect(__any(ps > kLazyW), 0)) {  // rare, as the mask above
+      // (measured on MI355X, both marked: 0.5-0.7% faster on both workloads)
       float mx = z[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = __builtin_elementwise_maximum(mx, z[e]);
